@@ -1,0 +1,164 @@
+/*
+ * parallax.h -- C ABI of libparallax.so, the gfx950 (MI355X) forward pass of
+ * Parallax attention.
+ *
+ * The operation.  For every query row i the library returns
+ *
+ *     o_i = o^SA_i - Sigma^(i)_KV rho_i
+ *
+ * where o^SA_i is standard softmax attention of q_i over its keys/values,
+ * Sigma^(i)_KV is the KV covariance under query i's softmax weights, and
+ * rho_i is the learned probe of the row (gist.science technical summary of
+ * Parallax, "Method: Parallax / core mechanism", output equation).  The
+ * boundary-amplification factor is fixed at zero (same page, "key design
+ * choices"; news.chathome.org article, "How does the mechanism work?"), so no
+ * other term is added.  A zero probe gives softmax attention exactly (the
+ * news.chathome.org article, "How does the mechanism work?").
+ *
+ * Conventions that the pages leave open (readings):
+ *   - Sigma^(i)_KV[a][b] = sum_j p_ij (v_j[a] - mean_v[a]) (k_j[b] - mean_k[b]):
+ *     population form, rows index the value coordinate, columns the key
+ *     coordinate, so rho has the head dimension d of the keys.
+ *   - The softmax scale multiplies q.k only; rho.k is not scaled.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).  rho has one probe per
+ *     query head.
+ *   - Prefill is causal: token t attends keys 0..t, the diagonal included.
+ *   - Decode: the query attends every cached key of its sequence (its own
+ *     key/value already appended).  An empty sequence returns zeros.
+ *
+ * Computation.  Both entry points stream K/V once (news.chathome.org article,
+ * "Hardware argument"; gist.science summary, "Hardware-aware algorithm"):
+ * the softmax branch and the probe branch share the K/V tiles, the running
+ * max and the rescale factors.  The kernels accumulate
+ *     l = sum_j P_j,  A = sum_j P_j v_j,  B = sum_j P_j r_j v_j,  c = sum_j P_j r_j
+ * with P_j = exp(s_j - m), r_j = <rho, k_j>, and finish with
+ *     o = A/l - (B/l - (c/l) A/l)
+ * which equals the covariance form.  Accumulation is fp32.
+ *
+ * Memory.  Every pointer argument named as "device" is device memory owned by
+ * the caller; the library never allocates, frees or synchronises.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
+ * return as soon as the kernels are queued.  A device fault surfaces at the
+ * caller's next synchronisation.  All tensors are dense, row-major, with the
+ * head dimension innermost, and start on a 16-byte boundary (cu_seqlens: 8
+ * bytes).  `out` must not overlap any input.  The library
+ * is stateless and re-entrant; concurrent calls are safe if their `out` and
+ * `workspace` buffers differ.
+ *
+ * Errors.  Arguments are checked on the host before any HIP call; a rejected
+ * call returns its code and touches nothing.  After the launches,
+ * hipGetLastError() != hipSuccess returns PLX_ERR_HIP.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PLX_OK = 0,
+    PLX_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size, bad scale */
+    PLX_ERR_UNSUPPORTED = 2,         /* valid but not built: head dim, group size, dtype */
+    PLX_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below the size query */
+    PLX_ERR_HIP = 4                  /* a launch failed (hipGetLastError) */
+} plx_status_t;
+
+typedef enum {
+    PLX_DTYPE_F32 = 0,   /* IEEE float32 inputs and output */
+    PLX_DTYPE_BF16 = 1   /* bfloat16 inputs and output (round to nearest even) */
+} plx_dtype_t;
+
+/* A hipStream_t, passed as an opaque pointer so this header needs no HIP
+ * include.  NULL selects the null stream. */
+typedef void *plx_stream_t;
+
+/*
+ * Causal prefill (T query tokens over the same T keys).
+ *
+ *   q, rho, out : device, [B, Hq, T, d]
+ *   k, v        : device, [B, Hkv, T, d]
+ *   rho         : may be NULL, which selects the softmax-only kernel; its
+ *                 output is bitwise equal to that of a rho of all zeros.
+ *   softmax_scale: tau > 0 and finite (usually 1/sqrt(d)).
+ *   dtype       : PLX_DTYPE_BF16 or PLX_DTYPE_F32, shared by all tensors.
+ *
+ * Supported: d in {64, 128}; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8};
+ * B, T >= 1.  Offsets are 64-bit, so tensors may exceed 2^31 elements.
+ * Returns PLX_ERR_INVALID_ARGUMENT for null q/k/v/out, non-positive sizes,
+ * Hq not a multiple of Hkv or a bad scale; PLX_ERR_UNSUPPORTED for other d,
+ * group sizes or dtypes.
+ */
+plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v,
+                                  const void *rho, void *out,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                  int32_t d, float softmax_scale,
+                                  plx_dtype_t dtype, plx_stream_t stream);
+
+/*
+ * Bytes of device workspace parallax_fwd_decode needs for these sizes and
+ * this split setting (keys_per_split as passed to parallax_fwd_decode; 0 =
+ * the library's own choice).  Returns 0 when the call needs no workspace
+ * (a single split), and (size_t)-1 for arguments parallax_fwd_decode would
+ * reject.
+ */
+size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
+                                          int32_t d, int64_t max_ctx,
+                                          plx_dtype_t dtype,
+                                          int32_t keys_per_split);
+
+/*
+ * Decode: one query token per sequence over a KV cache.
+ *
+ *   q, rho, out : device, [B, Hq, d]; rho may be NULL (softmax only, bitwise
+ *                 equal to a zero probe).
+ *   k_cache, v_cache : device.
+ *       cu_seqlens == NULL: contiguous cache [B, Hkv, max_ctx, d]; every
+ *                 sequence has max_ctx keys.
+ *       cu_seqlens != NULL: device int64 [B + 1] token offsets, cu[0] = 0,
+ *                 non-decreasing; sequence b has L_b = cu[b+1] - cu[b] keys,
+ *                 stored as a slab [Hkv, L_b, d] that starts at element
+ *                 cu[b] * Hkv * d of k_cache / v_cache.  The caller promises
+ *                 L_b <= max_ctx (keys past max_ctx are not read) and a
+ *                 well-formed cu_seqlens (it lives on the device and is not
+ *                 checked).
+ *   max_ctx     : >= 0; the longest context.
+ *   keys_per_split: 0 lets the library choose; otherwise a multiple of 32 in
+ *                 [32, 2^20].  A sequence is cut into chunks of that many keys,
+ *                 one workgroup each, and the chunks are merged by a second
+ *                 kernel.  Any setting gives the same result up to fp32
+ *                 rounding.
+ *   workspace   : device, at least parallax_fwd_decode_workspace_size(...)
+ *                 bytes (may be NULL when that size is 0); holds the
+ *                 per-chunk partial results; contents are scratch.
+ *
+ * Supported: d in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; dtype BF16 (F32 is
+ * accepted as a debugging aid).  Errors as for prefill, plus
+ * PLX_ERR_WORKSPACE_TOO_SMALL.
+ */
+plx_status_t parallax_fwd_decode(const void *q, const void *rho,
+                                 const void *k_cache, const void *v_cache,
+                                 const int64_t *cu_seqlens, int64_t max_ctx,
+                                 void *out, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t d, float softmax_scale,
+                                 plx_dtype_t dtype, int32_t keys_per_split,
+                                 void *workspace, size_t workspace_bytes,
+                                 plx_stream_t stream);
+
+/* Keys per chunk that parallax_fwd_decode uses for keys_per_split == 0, or a
+ * negative plx_status_t value for rejected arguments. */
+int32_t parallax_fwd_decode_auto_split(int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t d, int64_t max_ctx);
+
+/* A static, human-readable name for a status code. */
+const char *parallax_status_string(plx_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

@@ -1,0 +1,44 @@
+"""Helpers for the GPU parity tests: tolerances, error metrics, and moving
+device tensors to the host for the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+# Tolerances of the method's acceptance bar: fp32 max-abs 1e-5; bf16 max-abs
+# 2e-2 and relative L2 5e-3, both against the fp64 oracle on the same rounded
+# inputs.
+TOL = {torch.float32: dict(max_abs=1e-5, rel_l2=None), torch.bfloat16: dict(max_abs=2e-2, rel_l2=5e-3)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host64(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 copy of a device tensor (bf16 and fp32 upcast exactly)."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = got.astype(np.float64) - ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    denom = float(np.linalg.norm(ref.ravel()))
+    rel = float(np.linalg.norm(diff.ravel()) / denom) if denom > 0 else float(np.linalg.norm(diff.ravel()))
+    return max_abs, rel
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype, what: str):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    max_abs, rel = errors(got, ref)
+    tol = TOL[dtype]
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= tol["max_abs"], f"{what}: max_abs {max_abs:.3e} > {tol['max_abs']}"
+    if tol["rel_l2"] is not None:
+        assert rel <= tol["rel_l2"], f"{what}: rel_l2 {rel:.3e} > {tol['rel_l2']}"
+    return max_abs, rel
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()

@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/parallax.h declares, and every rejected call returns its status code
+from the host-side checks (which run before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_attention_flash_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "parallax.h")
+
+BF16, F32 = N.PLX_DTYPE_BF16, N.PLX_DTYPE_F32
+INVALID, UNSUP, WS = N.PLX_ERR_INVALID_ARGUMENT, N.PLX_ERR_UNSUPPORTED, N.PLX_ERR_WORKSPACE_TOO_SMALL
+SIZE_MAX = (1 << 64) - 1
+
+# Fake, never dereferenced device addresses: every call below is rejected by
+# the host checks before anything reaches the GPU.
+P = [0x10000000 * (i + 1) for i in range(8)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(N.LIB_PATH):
+        from transformer_attention_flash_amd.build import build_library
+        build_library()
+    return N.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(parallax_\w+)\s*\(", text)))
+
+
+def test_header_and_exports_agree(lib):
+    declared = _declared_functions()
+    assert declared == sorted(N.EXPORTS)
+    out = os.popen(f"nm -D --defined-only {N.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\bT (parallax_\w+)", out)))
+    assert exported == declared
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert N.status_string(code)
+    assert N.status_string(99) == "unknown status"
+
+
+def prefill(lib, q=P[0], k=P[1], v=P[2], rho=P[3], out=P[4], B=1, Hq=4, Hkv=2, T=16, d=64, scale=0.125,
+            dtype=BF16):
+    return lib.parallax_fwd_prefill(q, k, v, rho, out, B, Hq, Hkv, T, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(T=-3), INVALID), (dict(Hq=0), INVALID),
+    (dict(Hkv=0), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(d=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(Hq=6, Hkv=2), UNSUP), (dict(Hq=32, Hkv=2), UNSUP),
+    (dict(dtype=7), UNSUP),
+    (dict(out=P[0]), INVALID),                 # out aliases q
+    (dict(out=P[1] + 64), INVALID),            # out overlaps k
+    (dict(q=P[0] + 2), INVALID), (dict(rho=P[3] + 8), INVALID), (dict(out=P[4] + 4), INVALID),  # alignment
+])
+def test_prefill_rejections(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def decode(lib, q=P[0], rho=P[1], k=P[2], v=P[3], cu=None, max_ctx=4096, out=P[4], B=2, Hq=4, Hkv=2, d=128,
+           scale=0.088, dtype=BF16, ks=0, ws=P[5], ws_bytes=1 << 30):
+    return lib.parallax_fwd_decode(q, rho, k, v, cu, max_ctx, out, B, Hq, Hkv, d, scale, dtype, ks, ws, ws_bytes,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
+    (dict(B=0), INVALID), (dict(max_ctx=-1), INVALID), (dict(Hq=5, Hkv=2), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(ks=16), INVALID), (dict(ks=48), INVALID), (dict(ks=-32), INVALID), (dict(ks=(1 << 20) + 32), INVALID),
+    (dict(d=32), UNSUP), (dict(Hq=48, Hkv=2), UNSUP), (dict(dtype=3), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(out=P[0] + 16), INVALID),            # out overlaps q
+    (dict(out=P[5]), INVALID),                 # out overlaps the workspace
+    (dict(k=P[2] + 2), INVALID), (dict(ws=P[5] + 8), INVALID), (dict(cu=P[6] + 4), INVALID),  # alignment
+])
+def test_decode_rejections(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_workspace_size(lib):
+    f = lib.parallax_fwd_decode_workspace_size
+    # single chunk: no workspace
+    assert f(2048, 16, 8, 128, 128, BF16, 0) == 0
+    assert f(4, 16, 8, 128, 100, BF16, 128) == 0
+    # explicit chunks: stats (3 floats, padded to 256 B) + A and B vectors
+    B, Hq, d, L, ks = 3, 8, 64, 1000, 64
+    n = -(-L // ks)
+    slots = B * Hq * n
+    stats = (slots * 3 * 4 + 255) // 256 * 256
+    assert f(B, Hq, 4, d, L, BF16, ks) == stats + slots * 2 * d * 4
+    assert f(B, Hq, 3, d, L, BF16, ks) == SIZE_MAX     # Hq % Hkv
+    assert f(B, Hq, 4, 80, L, BF16, ks) == SIZE_MAX    # head dim
+    assert f(B, Hq, 4, d, L, BF16, 40) == SIZE_MAX     # not a multiple of 32
+
+
+def test_decode_auto_split(lib):
+    f = lib.parallax_fwd_decode_auto_split
+    assert f(2048, 16, 8, 128, 128) == 256          # one chunk, no merge
+    assert f(64, 16, 8, 128, 4096) == 512           # 8 chunks x 512 (b, g) units
+    assert f(256, 16, 8, 128, 32768) == 4096
+    ks = f(2048, 32, 16, 64, 32768)
+    assert ks % 32 == 0 and 256 <= ks <= 4096
+    assert f(2, 6, 4, 128, 100) == -INVALID
+    assert f(2, 4, 2, 100, 100) == -UNSUP
+
+
+def test_product_does_not_use_the_oracle():
+    """Only tests, the smoke check and the benchmark's CPU leg may touch oracle/."""
+    pkg = os.path.join(ROOT, "transformer_attention_flash_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|parallax_oracle|[\"']oracle[/\"']",
+                                     text, flags=re.M), f

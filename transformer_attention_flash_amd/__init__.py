@@ -1,0 +1,11 @@
+"""Parallax attention forward on AMD MI355X (gfx950).
+
+The computation lives in libparallax.so (hand-written HIP kernels behind the
+C ABI of include/parallax.h); this package binds it with ctypes and offers
+seeded synthetic inputs.  PyTorch supplies device memory and streams only.
+"""
+from ._native import EXPORTS, LIB_PATH, ParallaxError, load as load_library
+from .api import decode, decode_auto_split, decode_workspace_size, prefill
+
+__all__ = ["prefill", "decode", "decode_workspace_size", "decode_auto_split", "ParallaxError", "LIB_PATH",
+           "EXPORTS", "load_library"]

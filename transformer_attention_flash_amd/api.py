@@ -1,0 +1,137 @@
+"""Python entry points over libparallax.so.
+
+These functions only marshal arguments: they check that the tensors are on
+the GPU, contiguous and of one dtype, allocate the output (and the decode
+workspace) with torch, and pass raw device pointers and torch's current
+stream to the C ABI.  Every step of the computation runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _native as N
+
+_DTYPES = {torch.bfloat16: N.PLX_DTYPE_BF16, torch.float32: N.PLX_DTYPE_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensors(dtype, **tensors):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _dtype_code(dtype) -> int:
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}; use bfloat16 or float32")
+    return _DTYPES[dtype]
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor] = None, *,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal Parallax prefill.  q, rho: [B, Hq, T, d]; k, v: [B, Hkv, T, d].
+
+    rho=None runs the softmax-only kernel.  scale defaults to 1/sqrt(d).
+    """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D [B, H, T, d]")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, T, d] matching q")
+    if rho is not None and rho.shape != q.shape:
+        raise ValueError("rho must have q's shape")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check_tensors(q.dtype, q=q, k=k, v=v, rho=rho, out=out)
+    code = _dtype_code(q.dtype)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = N.load().parallax_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out), B, Hq, Hkv, T, d,
+                                       scale, code, _stream(stream))
+    N.check(st, "parallax_fwd_prefill")
+    return out
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype=torch.bfloat16,
+                          keys_per_split: int = 0) -> int:
+    n = N.load().parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype),
+                                                     int(keys_per_split))
+    if n == (1 << 64) - 1:
+        raise N.ParallaxError(N.PLX_ERR_INVALID_ARGUMENT, "parallax_fwd_decode_workspace_size")
+    return int(n)
+
+
+def decode_auto_split(B: int, Hq: int, Hkv: int, d: int, max_ctx: int) -> int:
+    ks = N.load().parallax_fwd_decode_auto_split(B, Hq, Hkv, d, int(max_ctx))
+    if ks < 0:
+        raise N.ParallaxError(-ks, "parallax_fwd_decode_auto_split")
+    return int(ks)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: Optional[torch.Tensor] = None, *,
+           cu_seqlens: Optional[torch.Tensor] = None, max_ctx: Optional[int] = None,
+           num_kv_heads: Optional[int] = None, scale: Optional[float] = None, keys_per_split: int = 0,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Parallax decode: one query token per sequence.  q, rho: [B, Hq, d].
+
+    Contiguous cache: k_cache, v_cache [B, Hkv, L, d] (cu_seqlens None).
+    Ragged cache: cu_seqlens int64 [B + 1] on the GPU, k_cache / v_cache the
+    packed slabs (any shape, contiguous), num_kv_heads and max_ctx required.
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    if cu_seqlens is None:
+        if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != d:
+            raise ValueError("contiguous k_cache must be [B, Hkv, L, d]")
+        Hkv, L = k_cache.shape[1], k_cache.shape[2]
+        if max_ctx is not None and max_ctx != L:
+            raise ValueError("max_ctx must equal the cache length for a contiguous cache")
+        max_ctx = L
+    else:
+        if num_kv_heads is None or max_ctx is None:
+            raise ValueError("a ragged cache needs num_kv_heads and max_ctx")
+        Hkv = int(num_kv_heads)
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.shape != (B + 1,) or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be a GPU int64 tensor of B + 1 offsets")
+        if not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache differ in shape")
+    if rho is not None and rho.shape != q.shape:
+        raise ValueError("rho must have q's shape")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensors(q.dtype, q=q, rho=rho, k_cache=k_cache, v_cache=v_cache, out=out)
+    code = _dtype_code(q.dtype)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace_size(B, Hq, Hkv, d, max_ctx, q.dtype, keys_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = N.load().parallax_fwd_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
+                                      int(max_ctx), _ptr(out), B, Hq, Hkv, d, scale, code, int(keys_per_split),
+                                      _ptr(workspace), ws_bytes, _stream(stream))
+    N.check(st, "parallax_fwd_decode")
+    return out

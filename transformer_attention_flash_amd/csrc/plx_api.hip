@@ -1,0 +1,201 @@
+// plx_api.hip -- the extern "C" entry points of libparallax.so: argument
+// checks (host only, before any HIP call), split and workspace policy, and the
+// kernel launches on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/parallax.h"
+#include "plx_kernels.h"
+
+namespace {
+
+constexpr int32_t kMaxKeysPerSplit = 1 << 20;
+constexpr int64_t kMaxGrid = (int64_t{1} << 31) - 1;
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+size_t elem_bytes(plx_dtype_t t) { return t == PLX_DTYPE_BF16 ? 2 : 4; }
+
+// The kernels read and write 8-element vectors: every tensor must start on a
+// 16-byte boundary.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shape checks shared by both entry points.
+plx_status_t check_heads(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, float scale, plx_dtype_t dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || d < 1) return PLX_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARGUMENT;
+    if (!valid_scale(scale)) return PLX_ERR_INVALID_ARGUMENT;
+    if (dtype != PLX_DTYPE_BF16 && dtype != PLX_DTYPE_F32) return PLX_ERR_UNSUPPORTED;
+    if (!supported_dim(d) || !supported_group(Hq / Hkv)) return PLX_ERR_UNSUPPORTED;
+    return PLX_OK;
+}
+
+// Keys per chunk when the caller leaves it to the library.  Aim for about
+// 4096 wavefronts (16 per CU on 256 CUs) so that the memory system sees
+// enough loads in flight, with chunks of 256..4096 keys; contexts of up to
+// 256 keys stay in one chunk and skip the merge kernel.
+int32_t auto_keys_per_split(int64_t units, int64_t max_ctx) {
+    if (max_ctx <= 256) return 256;
+    const int64_t target = 4096;
+    int64_t want = (units * max_ctx + target - 1) / target;
+    int32_t ks = 256;
+    while (ks < want && ks < 4096) ks *= 2;
+    return ks;
+}
+
+struct DecodePlan {
+    int32_t keys_per_split;
+    int32_t n_split;
+    size_t stats_bytes;  // offset of the vector block
+    size_t bytes;        // total workspace
+};
+
+plx_status_t plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx, plx_dtype_t dtype,
+                         int32_t keys_per_split, DecodePlan *plan) {
+    plx_status_t st = check_heads(B, Hq, Hkv, d, 1.f, dtype);
+    if (st != PLX_OK) return st;
+    if (max_ctx < 0) return PLX_ERR_INVALID_ARGUMENT;
+    if (keys_per_split != 0 &&
+        (keys_per_split < 32 || keys_per_split > kMaxKeysPerSplit || keys_per_split % 32 != 0))
+        return PLX_ERR_INVALID_ARGUMENT;
+    const int64_t units = static_cast<int64_t>(B) * Hkv;
+    const int32_t ks = keys_per_split ? keys_per_split : auto_keys_per_split(units, max_ctx);
+    int64_t n_split = (max_ctx + ks - 1) / ks;
+    if (n_split < 1) n_split = 1;
+    if (units * n_split > kMaxGrid || static_cast<int64_t>(B) * Hq > kMaxGrid) return PLX_ERR_UNSUPPORTED;
+    plan->keys_per_split = ks;
+    plan->n_split = static_cast<int32_t>(n_split);
+    if (n_split == 1) {
+        plan->stats_bytes = 0;
+        plan->bytes = 0;
+    } else {
+        const size_t slots = static_cast<size_t>(B) * Hq * static_cast<size_t>(n_split);
+        plan->stats_bytes = (slots * 3 * sizeof(float) + 255) & ~size_t{255};
+        plan->bytes = plan->stats_bytes + slots * 2 * static_cast<size_t>(d) * sizeof(float);
+    }
+    return PLX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, const void *rho, void *out,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                                  float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
+    if (!q || !k || !v || !out) return PLX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(out))
+        return PLX_ERR_INVALID_ARGUMENT;
+    if (T < 1) return PLX_ERR_INVALID_ARGUMENT;
+    plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
+    if (st != PLX_OK) return st;
+    const int G = Hq / Hkv;
+    const bool bf16 = dtype == PLX_DTYPE_BF16;
+    const int bq = plx::prefill_block_positions(bf16, G);
+    const int64_t n_qblk = (static_cast<int64_t>(T) + bq - 1) / bq;
+    if (static_cast<int64_t>(B) * Hkv * n_qblk > kMaxGrid) return PLX_ERR_UNSUPPORTED;
+
+    const size_t es = elem_bytes(dtype);
+    const size_t q_bytes = static_cast<size_t>(B) * Hq * T * d * es;
+    const size_t kv_bytes = static_cast<size_t>(B) * Hkv * T * d * es;
+    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k, kv_bytes) ||
+        overlaps(out, q_bytes, v, kv_bytes) || overlaps(out, q_bytes, rho, q_bytes))
+        return PLX_ERR_INVALID_ARGUMENT;
+
+    plx::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.rho = rho;
+    p.out = out;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.T = T;
+    p.n_qblk = static_cast<int32_t>(n_qblk);
+    p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    const hipError_t e =
+        plx::launch_prefill(p, bf16, d, G, rho != nullptr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx,
+                                          plx_dtype_t dtype, int32_t keys_per_split) {
+    DecodePlan plan;
+    if (plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan) != PLX_OK) return ~size_t{0};
+    return plan.bytes;
+}
+
+int32_t parallax_fwd_decode_auto_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx) {
+    DecodePlan plan;
+    const plx_status_t st = plan_decode(B, Hq, Hkv, d, max_ctx, PLX_DTYPE_BF16, 0, &plan);
+    return st == PLX_OK ? plan.keys_per_split : -static_cast<int32_t>(st);
+}
+
+plx_status_t parallax_fwd_decode(const void *q, const void *rho, const void *k_cache, const void *v_cache,
+                                 const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype,
+                                 int32_t keys_per_split, void *workspace, size_t workspace_bytes,
+                                 plx_stream_t stream) {
+    if (!q || !k_cache || !v_cache || !out) return PLX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(workspace) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0)
+        return PLX_ERR_INVALID_ARGUMENT;
+    plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
+    if (st != PLX_OK) return st;
+    DecodePlan plan;
+    st = plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan);
+    if (st != PLX_OK) return st;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return PLX_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t es = elem_bytes(dtype);
+    const size_t q_bytes = static_cast<size_t>(B) * Hq * d * es;
+    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, rho, q_bytes) ||
+        overlaps(out, q_bytes, workspace, plan.bytes))
+        return PLX_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens) {
+        const size_t kv_bytes = static_cast<size_t>(B) * Hkv * static_cast<size_t>(max_ctx) * d * es;
+        if (overlaps(out, q_bytes, k_cache, kv_bytes) || overlaps(out, q_bytes, v_cache, kv_bytes))
+            return PLX_ERR_INVALID_ARGUMENT;
+    }
+
+    plx::DecodeParams p;
+    p.q = q;
+    p.rho = rho;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.cu = cu_seqlens;
+    p.max_ctx = max_ctx;
+    p.out = out;
+    p.ws_stats = plan.bytes ? static_cast<float *>(workspace) : nullptr;
+    p.ws_vec = plan.bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.stats_bytes) : nullptr;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.keys_per_split = plan.keys_per_split;
+    p.n_split = plan.n_split;
+    p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    const hipError_t e =
+        plx::launch_decode(p, dtype == PLX_DTYPE_BF16, d, Hq / Hkv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+const char *parallax_status_string(plx_status_t s) {
+    switch (s) {
+    case PLX_OK: return "ok";
+    case PLX_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PLX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PLX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PLX_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

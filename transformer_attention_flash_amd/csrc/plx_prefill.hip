@@ -1,0 +1,393 @@
+// plx_prefill.hip -- causal Parallax attention prefill on gfx950.
+//
+// A workgroup of 4 wavefronts owns one (sequence b, KV head g, query block)
+// tile: 128 query rows = the G query heads that share KV head g at 128/G
+// consecutive positions.  Each wavefront owns 32 of those rows as two
+// 16-column MFMA tiles.  K/V tiles of KT keys are staged once in LDS
+// (double-buffered) and shared by every row of the workgroup and by both
+// scoring branches (the news.chathome.org article on Parallax, "Hardware
+// argument": the two branches share the online max, the scaling factors and
+// the K and V tiles; the gist.science summary, "Hardware-aware algorithm").
+//
+// Per key tile and 16-row column tile a wavefront issues
+//   S^T = K q^T and R^T = K rho^T       (the same K operand registers),
+//   A^T += V^T P^T and B^T += V^T (P*R)^T (the same V operand registers),
+// with P = 2^(s*log2e - m) from the running max m of the query row, shared
+// by the probe branch, and the same rescale factor applied to A, B, l and c.
+// The probe rows thus ride in the same MFMA stream as the query rows (the
+// probe tile is the query tile's neighbour in the N dimension); the softmax
+// state is computed once.  The epilogue forms o = A/l - (B/l - (c/l) A/l).
+//
+// LDS layouts:
+//   K  [KT][D + pad]  natural rows; a lane's A operand is 8 contiguous dims.
+//   Vt [D][KT + pad]  transposed, with the keys of each 32-key slice permuted
+//                     so that the 8 keys a lane needs for one value operand
+//                     are contiguous: key 16*blk + 4*q + i (blk = 16-key block
+//                     of the score tile, q = lane group, i = C-tile row) sits
+//                     at position 32*(blk/2) + 8*q + 4*(blk%2) + i.  The
+//                     loader transposes 4-key x 8-dim blocks in registers.
+// The softmax-only kernel (no probe) is the same template with the probe
+// branch compiled out; it runs the query-side arithmetic in the same order,
+// so a zero probe reproduces its output bit for bit.
+#include "plx_device.h"
+#include "plx_kernels.h"
+
+namespace plx {
+
+namespace {
+
+template <class T> struct PrefillCfg;
+template <> struct PrefillCfg<BF16> {
+    static constexpr int KT = 64;  // keys per LDS tile
+};
+template <> struct PrefillCfg<F32> {
+    static constexpr int KT = 32;
+};
+
+constexpr int kPrefillWaves = 4;
+constexpr int kColTiles = 2;  // 16-row column tiles per wavefront
+
+// Four Op8 rows (keys 4r .. 4r+3 of one 8-dim chunk) -> element e of each, as
+// the 4 contiguous LDS entries of transposed row e.
+__device__ __forceinline__ void store_vt4(uint16_t *dst, const Op8<BF16> (&v)[4], int e) {
+    const uint32_t w0 = half_lo(v[0].w[e >> 1], e) | half_hi(v[1].w[e >> 1], e);
+    const uint32_t w1 = half_lo(v[2].w[e >> 1], e) | half_hi(v[3].w[e >> 1], e);
+    *reinterpret_cast<u32x2 *>(dst) = u32x2{w0, w1};
+}
+__device__ __forceinline__ void store_vt4(float *dst, const Op8<F32> (&v)[4], int e) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
+}
+
+__device__ __forceinline__ void store_op8(uint16_t *dst, const Op8<BF16> &o) {
+    *reinterpret_cast<u32x4 *>(dst) = o.w;
+}
+__device__ __forceinline__ void store_op8(float *dst, const Op8<F32> &o) {
+    reinterpret_cast<f32x4 *>(dst)[0] = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+    reinterpret_cast<f32x4 *>(dst)[1] = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
+}
+
+__device__ __forceinline__ void store4(uint16_t *dst, const float (&y)[4]) {
+    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
+}
+__device__ __forceinline__ void store4(float *dst, const float (&y)[4]) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+}
+
+}  // namespace
+
+template <class T, int D, int G, bool HAS_RHO>
+__global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillParams p) {
+    using S = typename T::storage;
+    constexpr int KT = PrefillCfg<T>::KT;
+    constexpr int NB = kColTiles;
+    constexpr int PW = 16 * NB / G;          // positions per wavefront
+    constexpr int BQ = PW * kPrefillWaves;   // positions per workgroup
+    constexpr int KS = D / 32;               // contraction slices over the head dim
+    constexpr int NKB = KT / 16;             // 16-key blocks per tile
+    constexpr int NU = KT / 32;              // 32-key slices for the value GEMMs
+    constexpr int DT = D / 16;               // 16-dim output tiles
+    constexpr int PAD = 16 / sizeof(S);      // one 16-byte bank group of padding
+    constexpr int KRS = D + PAD;             // K row stride (elements)
+    constexpr int VRS = KT + PAD;            // Vt row stride (elements)
+    constexpr int NTHR = kPrefillWaves * kWave;
+    constexpr int KCH = KT * D / 8;          // 8-element K chunks per tile
+    constexpr int NKC = (KCH + NTHR - 1) / NTHR;
+    constexpr int VRUN = (KT / 4) * (D / 8); // 4-key x 8-dim V blocks per tile
+    constexpr int NVR = (VRUN + NTHR - 1) / NTHR;
+    static_assert(16 * NB % G == 0, "group size must divide the wave's rows");
+
+    __shared__ __attribute__((aligned(16))) S lds_k[2][KT * KRS];
+    __shared__ __attribute__((aligned(16))) S lds_v[2][D * VRS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    // Longest query blocks first: they have the most key tiles.
+    const int n_units = p.B * p.Hkv;
+    const int id = blockIdx.x;
+    const int qb = p.n_qblk - 1 - id / n_units;
+    const int unit = id % n_units;
+    const int b = unit / p.Hkv;
+    const int g = unit % p.Hkv;
+    const int T_len = p.T;
+
+    const int pos0 = qb * BQ;
+    const int wpos0 = pos0 + wave * PW;
+    const int wpos_last = wpos0 + PW - 1;
+    const int key_end = min(pos0 + BQ, T_len);  // keys this workgroup ever needs
+    const int n_tiles = (key_end + KT - 1) / KT;
+
+    const int64_t kv_base = (static_cast<int64_t>(b) * p.Hkv + g) * T_len * static_cast<int64_t>(D);
+    const S *kg = static_cast<const S *>(p.k) + kv_base;
+    const S *vg = static_cast<const S *>(p.v) + kv_base;
+
+    // This lane's rows: column tile nb, column col -> row r = 16*nb + col of
+    // the wavefront, position wpos0 + r / G, query head g*G + r % G.
+    int pos[NB];
+    int64_t qoff[NB];
+    Op8<T> qop[NB][KS];
+    Op8<T> rop[NB][HAS_RHO ? KS : 1];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = 16 * nb + col;
+        pos[nb] = wpos0 + r / G;
+        const int head = g * G + r % G;
+        qoff[nb] = ((static_cast<int64_t>(b) * p.Hq + head) * T_len + min(pos[nb], T_len - 1)) * D;
+        const S *qrow = static_cast<const S *>(p.q) + qoff[nb];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qop[nb][s] = op8_load(qrow + 32 * s + 8 * grp);
+        if constexpr (HAS_RHO) {
+            const S *rrow = static_cast<const S *>(p.rho) + qoff[nb];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) rop[nb][s] = op8_load(rrow + 32 * s + 8 * grp);
+        }
+    }
+
+    // Loader registers for one tile.
+    Op8<T> kreg[NKC];
+    Op8<T> vreg[NVR][4];
+    auto load_tile = [&](int j) {
+        const int key0 = j * KT;
+#pragma unroll
+        for (int n = 0; n < NKC; ++n) {
+            const int c = tid + n * NTHR;
+            if (c < KCH) {
+                const int key = c / (D / 8);
+                const int off = (c % (D / 8)) * 8;
+                const int kk = min(key0 + key, T_len - 1);
+                kreg[n] = op8_load(kg + static_cast<int64_t>(kk) * D + off);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVR; ++n) {
+            const int it = tid + n * NTHR;
+            if (it < VRUN) {
+                const int chunk = it % (D / 8);
+                const int run = it / (D / 8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kk = min(key0 + 4 * run + i, T_len - 1);
+                    vreg[n][i] = op8_load(vg + static_cast<int64_t>(kk) * D + chunk * 8);
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < NKC; ++n) {
+            const int c = tid + n * NTHR;
+            if (c < KCH) {
+                const int key = c / (D / 8);
+                const int off = (c % (D / 8)) * 8;
+                store_op8(&lds_k[buf][key * KRS + off], kreg[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVR; ++n) {
+            const int it = tid + n * NTHR;
+            if (it < VRUN) {
+                const int chunk = it % (D / 8);
+                const int run = it / (D / 8);
+                const int blk = run >> 2, q = run & 3;
+                const int vpos = 32 * (blk >> 1) + 8 * q + 4 * (blk & 1);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) store_vt4(&lds_v[buf][(chunk * 8 + e) * VRS + vpos], vreg[n], e);
+            }
+        }
+    };
+
+    float m_run[NB], lsum[NB], csum[NB];
+    f32x4 acc_a[NB][DT];
+    f32x4 acc_b[NB][HAS_RHO ? DT : 1];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = -INFINITY;
+        lsum[nb] = 0.f;
+        csum[nb] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            acc_a[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_RHO) acc_b[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    load_tile(0);
+    store_tile(0);
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int buf = j & 1;
+        __syncthreads();  // tile j is in lds[buf]; everyone is done with lds[buf ^ 1]
+        const bool more = j + 1 < n_tiles;
+        if (more) load_tile(j + 1);
+
+        const int key0 = j * KT;
+        if (key0 <= wpos_last) {
+            const bool diag = key0 + KT - 1 > wpos0;
+            const S *kt = lds_k[buf];
+            const S *vt = lds_v[buf];
+
+            f32x4 sacc[NB][NKB];
+            f32x4 racc[NB][HAS_RHO ? NKB : 1];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Op8<T> kop[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) kop[s] = op8_load(kt + (16 * kb + col) * KRS + 32 * s + 8 * grp);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) a = mma32(kop[s], qop[nb][s], a);
+                    sacc[nb][kb] = a;
+                    if constexpr (HAS_RHO) {
+                        f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < KS; ++s) r = mma32(kop[s], rop[nb][s], r);
+                        racc[nb][kb] = r;
+                    }
+                }
+            }
+
+            Op8<T> pop[NB][NU];
+            Op8<T> prop[NB][HAS_RHO ? NU : 1];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float x[NKB * 4];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < NKB * 4; ++e) {
+                    const int key = key0 + 16 * (e >> 2) + 4 * grp + (e & 3);
+                    float v = sacc[nb][e >> 2][e & 3] * p.scale_log2;
+                    if (diag && key > pos[nb]) v = -INFINITY;
+                    x[e] = v;
+                    mt = fmaxf(mt, v);
+                }
+                mt = group_max(mt);
+                const float m_new = fmaxf(m_run[nb], mt);
+                const float alpha = fast_exp2(m_run[nb] - m_new);
+                m_run[nb] = m_new;
+                float ps = 0.f, cs = 0.f;
+                float pr[NKB * 4];
+#pragma unroll
+                for (int e = 0; e < NKB * 4; ++e) {
+                    x[e] = fast_exp2(x[e] - m_new);
+                    ps += x[e];
+                    if constexpr (HAS_RHO) {
+                        pr[e] = x[e] * racc[nb][e >> 2][e & 3];
+                        cs += pr[e];
+                    }
+                }
+                lsum[nb] = alpha * lsum[nb] + ps;
+                if constexpr (HAS_RHO) csum[nb] = alpha * csum[nb] + cs;
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    acc_a[nb][t] *= alpha;
+                    if constexpr (HAS_RHO) acc_b[nb][t] *= alpha;
+                }
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = x[8 * u + e];
+                    pop[nb][u] = op8_pack(w, T{});
+                    if constexpr (HAS_RHO) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[e] = pr[8 * u + e];
+                        prop[nb][u] = op8_pack(w, T{});
+                    }
+                }
+            }
+
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const Op8<T> vop = op8_load(vt + (16 * t + col) * VRS + 32 * u + 8 * grp);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc_a[nb][t] = mma32(vop, pop[nb][u], acc_a[nb][t]);
+                        if constexpr (HAS_RHO) acc_b[nb][t] = mma32(vop, prop[nb][u], acc_b[nb][t]);
+                    }
+                }
+            }
+        }
+
+        if (more) store_tile(buf ^ 1);
+    }
+
+    // Epilogue: acc[nb][t][i] is head-dim 16*t + 4*grp + i of this lane's row.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l = group_sum(lsum[nb]);
+        const float c = HAS_RHO ? group_sum(csum[nb]) : 0.f;
+        if (pos[nb] < T_len) {
+            const float inv = 1.f / l;
+            const float cbar = c * inv;
+            S *o = static_cast<S *>(p.out) + qoff[nb];
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float osa = acc_a[nb][t][i] * inv;
+                    if constexpr (HAS_RHO) {
+                        const float corr = acc_b[nb][t][i] * inv - cbar * osa;
+                        y[i] = osa - corr;
+                    } else {
+                        y[i] = osa;
+                    }
+                }
+                store4(o + 16 * t + 4 * grp, y);
+            }
+        }
+    }
+}
+
+namespace {
+
+template <class T, int D, int G, bool R>
+hipError_t launch_prefill_r(const PrefillParams &p, hipStream_t stream) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.Hkv * p.n_qblk;
+    hipLaunchKernelGGL((prefill_kernel<T, D, G, R>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kPrefillWaves * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <class T, int D, int G>
+hipError_t launch_prefill_g(const PrefillParams &p, bool has_rho, hipStream_t stream) {
+    return has_rho ? launch_prefill_r<T, D, G, true>(p, stream) : launch_prefill_r<T, D, G, false>(p, stream);
+}
+
+template <class T, int D>
+hipError_t launch_prefill_d(const PrefillParams &p, int G, bool has_rho, hipStream_t stream) {
+    switch (G) {
+    case 1: return launch_prefill_g<T, D, 1>(p, has_rho, stream);
+    case 2: return launch_prefill_g<T, D, 2>(p, has_rho, stream);
+    case 4: return launch_prefill_g<T, D, 4>(p, has_rho, stream);
+    case 8: return launch_prefill_g<T, D, 8>(p, has_rho, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class T>
+hipError_t launch_prefill_t(const PrefillParams &p, int D, int G, bool has_rho, hipStream_t stream) {
+    switch (D) {
+    case 64: return launch_prefill_d<T, 64>(p, G, has_rho, stream);
+    case 128: return launch_prefill_d<T, 128>(p, G, has_rho, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int prefill_block_positions(bool /*bf16*/, int G) { return 16 * kColTiles / G * kPrefillWaves; }
+
+hipError_t launch_prefill(const PrefillParams &p, bool bf16, int D, int G, bool has_rho, hipStream_t stream) {
+    return bf16 ? launch_prefill_t<BF16>(p, D, G, has_rho, stream)
+                : launch_prefill_t<F32>(p, D, G, has_rho, stream);
+}
+
+}  // namespace plx
