@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax attention forward on one MI355X.
+
+One JSON line on stdout.  The headline (`value`) is decode KV HBM throughput
+on the decode workload (B=64, Hq=16, Hkv=8, d=128, 4096 cached keys per
+sequence, bf16): one step is one call of parallax_fwd_decode over the whole
+batch (split-KV kernel + merge kernel).  The second half of the metric, the
+causal prefill (B=8, T=4096, Hq=16, Hkv=8, d=128, bf16), is timed the same way
+and reported under "prefill" with its MFMA roofline.
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Several input sets are rotated so that no step finds its K/V in the 256 MB
+Infinity Cache.  Kernel time is measured with HIP events recorded on the
+stream the kernels run on (torch's current stream, which the binding passes
+to the C ABI).  The CPU baseline is the fp64 oracle, as it stands, on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+DECODE_WL = "decode_bf16_b64_hq16_hkv8_l4096_d128"
+PREFILL_WL = "prefill_bf16_b8_hq16_hkv8_t4096_d128"
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_traffic.md")
+DECODE_SOURCES = ["transformer_attention_flash_amd/csrc/plx_decode.hip",
+                  "transformer_attention_flash_amd/csrc/plx_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(digest: str):
+    """HBM bytes per decode launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m and f and w) or m.group(1) != digest:
+        return None
+    return float(f.group(1)) + float(w.group(1))
+
+
+def time_steps(fn_for_step, steps, warmup, torch):
+    """Run warmup steps, then time `steps` steps with HIP events on the current
+    stream; returns (total seconds by events, per-step list of ms)."""
+    for i in range(warmup):
+        fn_for_step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        fn_for_step(warmup + i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / 1e3, per
+
+
+def cpu_baseline_decode(x, w, budget_s: float):
+    """Oracle (expanded form) on whole sequences of the decode workload, in
+    passes over the batch, until about budget_s seconds of CPU work; returns
+    the oracle's KV GB/s."""
+    import numpy as np
+    import oracle  # the CPU baseline leg of the benchmark
+
+    tau = 1.0 / math.sqrt(w.d)
+    per_seq_bytes = 2 * 2 * w.Hkv * w.L * w.d
+    chunks = []
+    for b in range(0, w.B, 8):  # host fp64 copies, 8 sequences per oracle call
+        sl = slice(b, min(b + 8, w.B))
+        chunks.append(tuple(x[n][sl].float().cpu().numpy().astype(np.float64) for n in ("q", "rho", "k", "v")))
+    done_bytes, spent, nseq, passes = 0, 0.0, 0, 0
+    while spent < budget_s:
+        for q, r, k, v in chunks:
+            t0 = time.perf_counter()
+            oracle.decode(q, r, k, v, tau, form=oracle.EXPANDED)
+            spent += time.perf_counter() - t0
+            nseq += q.shape[0]
+            done_bytes += q.shape[0] * per_seq_bytes
+        passes += 1
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{passes} pass(es) over all {w.B} sequences ({w.Hq} heads, {w.L} keys each; {nseq} "
+                      f"sequence evaluations), fp64 expanded form, {spent:.1f} s"}
+
+
+def cpu_baseline_prefill(x, w, budget_s: float):
+    """Oracle on query rows of the prefill workload (whole sequences, all
+    heads, positions visited in a strided order) until about budget_s seconds;
+    returns the oracle's TFLOP/s under the GPU's flop count (8 d flops per
+    causal pair)."""
+    import numpy as np
+    import oracle
+
+    tau = 1.0 / math.sqrt(w.d)
+    flops, spent, nrows, nseq = 0.0, 0.0, 0, 0
+    step = 64
+    for b in range(w.B):
+        if spent >= budget_s:
+            break
+        q, r, k, v = (x[n][b:b + 1].float().cpu().numpy().astype(np.float64) for n in ("q", "rho", "k", "v"))
+        nseq += 1
+        for off in range(step):
+            if spent >= budget_s:
+                break
+            ts = np.arange(off, w.T, step)
+            rows = np.array([(0, h, t) for h in range(w.Hq) for t in ts], dtype=np.int64)
+            t0 = time.perf_counter()
+            oracle.prefill(q, k, v, r, tau, form=oracle.EXPANDED, rows=rows)
+            spent += time.perf_counter() - t0
+            nrows += len(rows)
+            flops += float(8 * w.d * (rows[:, 2] + 1).sum())
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{nrows} query rows from {nseq} sequence(s) (all {w.Hq} heads, positions over "
+                      f"0..{w.T - 1}), fp64 expanded form, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Parallax forward here runs on a single MI355X with no "
+              "cross-GPU sharding; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_attention_flash_amd as plx
+    from transformer_attention_flash_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    plx.load_library()
+    dev = "cuda"
+
+    if args.copy_probe_mib:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+        # calibrate the per-kernel HBM traffic of the same profiling run.
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
+
+    # ---------------- decode (headline) ----------------
+    w = synth.WORKLOADS[DECODE_WL]
+    log(f"decode workload {w.name}: generating {args.sets} input sets")
+    sets = [synth.make_decode(w.B, w.Hq, w.Hkv, w.L, w.d, w.dtype, dev, seed=s) for s in range(args.sets)]
+    out = torch.empty_like(sets[0]["q"])
+    ks = plx.decode_auto_split(w.B, w.Hq, w.Hkv, w.d, w.L)
+    ws = torch.empty(max(plx.decode_workspace_size(w.B, w.Hq, w.Hkv, w.d, w.L), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def decode_step(i):
+        x = sets[i % len(sets)]
+        plx.decode(x["q"], x["k"], x["v"], x["rho"], out=out, workspace=ws)
+
+    secs, per = time_steps(decode_step, args.steps, args.warmup, torch)
+    kv_bytes = 2 * 2 * w.B * w.Hkv * w.L * w.d
+    qro_bytes = 3 * 2 * w.B * w.Hq * w.d
+    step_s = secs / args.steps
+    gbs = kv_bytes / step_s / 1e9
+    flops = 4 * 2 * w.d * w.B * w.Hq * w.L
+    digest = source_digest(DECODE_SOURCES)
+    traffic = read_traffic(digest)
+    log(f"decode: {step_s * 1e6:.1f} us/step, {gbs:.0f} GB/s KV, keys_per_split={ks}")
+
+    result = {
+        "metric": "decode KV HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "context": w.L,
+                   "keys_per_split": ks, "input_sets_rotated": args.sets, "accumulate": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": "decode_split_kernel + decode_combine_kernel (one parallax_fwd_decode call)",
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "kernel_source_digest": digest},
+        "decode_detail": {"us_per_step_median": round(sorted(per)[len(per) // 2] * 1e3, 2),
+                          "us_per_step_p10": round(sorted(per)[len(per) // 10] * 1e3, 2),
+                          "us_per_step_p90": round(sorted(per)[(9 * len(per)) // 10] * 1e3, 2),
+                          "tokens_per_s": round(w.B / step_s, 1),
+                          "kv_plus_q_rho_out_GBs": round((kv_bytes + qro_bytes) / step_s / 1e9, 2),
+                          "tflops": round(flops / step_s / 1e12, 3)},
+    }
+
+    if not args.no_cpu_baseline:
+        log("decode CPU baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_decode(sets[0], w, args.cpu_budget)
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill ----------------
+    if not args.no_prefill:
+        pw = synth.WORKLOADS[PREFILL_WL]
+        log(f"prefill workload {pw.name}")
+        psets = [synth.make_prefill(pw.B, pw.Hq, pw.Hkv, pw.T, pw.d, pw.dtype, dev, seed=s) for s in range(2)]
+        pout = torch.empty_like(psets[0]["q"])
+
+        def prefill_step(i):
+            x = psets[i % len(psets)]
+            plx.prefill(x["q"], x["k"], x["v"], x["rho"], out=pout)
+
+        def softmax_only_step(i):
+            x = psets[i % len(psets)]
+            plx.prefill(x["q"], x["k"], x["v"], None, out=pout)
+
+        psecs, pper = time_steps(prefill_step, args.prefill_steps, 2, torch)
+        pairs = pw.B * pw.Hq * pw.T * (pw.T + 1) // 2
+        pflops = 4 * 2 * pw.d * pairs
+        tf = pflops / (psecs / args.prefill_steps) / 1e12
+        ssecs, _ = time_steps(softmax_only_step, args.prefill_steps, 2, torch)
+        stf = 2 * 2 * pw.d * pairs / (ssecs / args.prefill_steps) / 1e12
+        log(f"prefill: {psecs / args.prefill_steps * 1e3:.3f} ms/step, {tf:.1f} TFLOP/s; softmax-only "
+            f"{ssecs / args.prefill_steps * 1e3:.3f} ms, {stf:.1f} TFLOP/s")
+        result["prefill"] = {
+            "workload": pw.name, "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(psecs / args.prefill_steps * 1e3, 4), "steps": args.prefill_steps,
+            "tokens_per_s": round(pw.B * pw.T / (psecs / args.prefill_steps), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prefill_kernel<bf16, 128, 2, rho>",
+                         "algorithmic_flops_per_launch": pflops},
+            "softmax_only": {"value": round(stf, 2), "unit": "TFLOP/s",
+                             "ms_per_step": round(ssecs / args.prefill_steps * 1e3, 4)},
+        }
+        if not args.no_cpu_baseline:
+            log("prefill CPU baseline (oracle)")
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,6 +34,10 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype, what: str):
     max_abs, rel = errors(got, ref)
     tol = TOL[dtype]
     say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    if got.size:
+        i = np.unravel_index(int(np.abs(got - ref).argmax()), got.shape)
+        say(f"    worst element at {tuple(int(j) for j in i)}: got {got[i]!r} oracle {ref[i]!r}; "
+            f"max |oracle| {float(np.abs(ref).max()):.3f}")
     assert max_abs <= tol["max_abs"], f"{what}: max_abs {max_abs:.3e} > {tol['max_abs']}"
     if tol["rel_l2"] is not None:
         assert rel <= tol["rel_l2"], f"{what}: rel_l2 {rel:.3e} > {tol['rel_l2']}"

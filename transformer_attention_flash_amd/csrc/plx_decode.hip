@@ -223,17 +223,15 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeParams p) {
         // query column of the same head, G lanes to their left.
         const float alpha_q = row_shr<G>(alpha_own);
         float pv[8];
-        float tsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float pf = row_shr<G>(pq[e]);
             pv[e] = is_q ? pq[e] : (is_r ? pf * x[e] : 0.f);
-            tsum += pv[e];
         }
         const float alpha = is_q ? alpha_own : (is_r ? alpha_q : 1.f);
-        rsum = alpha * rsum + tsum;
-
         const Op8<T> pop = op8_pack(pv, T{});
+        rsum = alpha * rsum + op8_sum(pop);
+
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             acc[t] *= alpha;

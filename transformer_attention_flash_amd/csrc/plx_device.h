@@ -115,6 +115,26 @@ __device__ __forceinline__ Op8<F32> op8_pack(const float (&x)[8], F32) {
     return o;
 }
 
+// Sum of the 8 operand values exactly as the MFMA sees them (after rounding to
+// bf16).  Row sums taken over these values make the weights that multiply V
+// sum exactly to the normaliser, so rounding perturbs the weights but not
+// their total.
+__device__ __forceinline__ float op8_sum(const Op8<BF16> &o) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        s += __builtin_bit_cast(float, o.w[j] << 16);
+        s += __builtin_bit_cast(float, o.w[j] & 0xffff0000u);
+    }
+    return s;
+}
+__device__ __forceinline__ float op8_sum(const Op8<F32> &o) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += o.v[e];
+    return s;
+}
+
 // 16-bit element `e` of a packed bf16 pair word, as the low or high half.
 __device__ __forceinline__ uint32_t half_lo(uint32_t w, int e) { return (e & 1) ? (w >> 16) : (w & 0xffffu); }
 __device__ __forceinline__ uint32_t half_hi(uint32_t w, int e) { return (e & 1) ? (w & 0xffff0000u) : (w << 16); }

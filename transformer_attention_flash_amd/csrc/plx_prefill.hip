@@ -269,15 +269,26 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
                 const float m_new = fmaxf(m_run[nb], mt);
                 const float alpha = fast_exp2(m_run[nb] - m_new);
                 m_run[nb] = m_new;
-                float ps = 0.f, cs = 0.f;
                 float pr[NKB * 4];
 #pragma unroll
                 for (int e = 0; e < NKB * 4; ++e) {
                     x[e] = fast_exp2(x[e] - m_new);
-                    ps += x[e];
+                    if constexpr (HAS_RHO) pr[e] = x[e] * racc[nb][e >> 2][e & 3];
+                }
+                // Row sums over the rounded operands (see op8_sum).
+                float ps = 0.f, cs = 0.f;
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = x[8 * u + e];
+                    pop[nb][u] = op8_pack(w, T{});
+                    ps += op8_sum(pop[nb][u]);
                     if constexpr (HAS_RHO) {
-                        pr[e] = x[e] * racc[nb][e >> 2][e & 3];
-                        cs += pr[e];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[e] = pr[8 * u + e];
+                        prop[nb][u] = op8_pack(w, T{});
+                        cs += op8_sum(prop[nb][u]);
                     }
                 }
                 lsum[nb] = alpha * lsum[nb] + ps;
@@ -286,18 +297,6 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
                 for (int t = 0; t < DT; ++t) {
                     acc_a[nb][t] *= alpha;
                     if constexpr (HAS_RHO) acc_b[nb][t] *= alpha;
-                }
-#pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    float w[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) w[e] = x[8 * u + e];
-                    pop[nb][u] = op8_pack(w, T{});
-                    if constexpr (HAS_RHO) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) w[e] = pr[8 * u + e];
-                        prop[nb][u] = op8_pack(w, T{});
-                    }
                 }
             }
 
