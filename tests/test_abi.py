@@ -111,11 +111,12 @@ def test_decode_workspace_size(lib):
 
 def test_decode_auto_split(lib):
     f = lib.parallax_fwd_decode_auto_split
-    assert f(2048, 16, 8, 128, 128) == 256          # one chunk, no merge
-    assert f(64, 16, 8, 128, 4096) == 512           # 8 chunks x 512 (b, g) units
+    assert f(2048, 16, 8, 128, 128) == 128          # one chunk, no merge
+    assert f(2, 16, 8, 128, 200) == 256
+    assert f(64, 16, 8, 128, 4096) == 4096          # one chunk per (b, g): no merge kernel
+    assert f(1, 16, 8, 128, 4096) == 512            # few sequences: more, smaller chunks
     assert f(256, 16, 8, 128, 32768) == 4096
-    ks = f(2048, 32, 16, 64, 32768)
-    assert ks % 32 == 0 and 256 <= ks <= 4096
+    assert f(2048, 32, 16, 64, 32768) == 4096
     assert f(2, 6, 4, 128, 100) == -INVALID
     assert f(2, 4, 2, 100, 100) == -UNSUP
 

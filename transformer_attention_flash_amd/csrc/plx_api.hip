@@ -37,16 +37,20 @@ plx_status_t check_heads(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, float sc
     return PLX_OK;
 }
 
-// Keys per chunk when the caller leaves it to the library.  Aim for about
-// 4096 wavefronts (16 per CU on 256 CUs) so that the memory system sees
-// enough loads in flight, with chunks of 256..4096 keys; contexts of up to
-// 256 keys stay in one chunk and skip the merge kernel.
+// Keys per chunk when the caller leaves it to the library.  A chunk is one
+// workgroup of up to 8 wavefronts (one per 128 keys) that merge their states
+// in LDS, so large chunks are cheap; chunks stay as large as possible
+// (up to 4096 keys, which needs no merge kernel for contexts up to 4096)
+// while keeping at least 512 workgroups (2 per CU) in flight.  Contexts of
+// up to 256 keys stay in one chunk.
 int32_t auto_keys_per_split(int64_t units, int64_t max_ctx) {
-    if (max_ctx <= 256) return 256;
-    const int64_t target = 4096;
-    int64_t want = (units * max_ctx + target - 1) / target;
-    int32_t ks = 256;
-    while (ks < want && ks < 4096) ks *= 2;
+    if (max_ctx <= 256) {  // one chunk, rounded up to a power of two
+        int32_t ks = 32;
+        while (ks < max_ctx) ks *= 2;
+        return ks;
+    }
+    int32_t ks = 4096;
+    while (ks > 512 && units * ((max_ctx + ks - 1) / ks) < 512) ks /= 2;
     return ks;
 }
 

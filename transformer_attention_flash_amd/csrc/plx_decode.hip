@@ -119,14 +119,21 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams &p, int b) {
 
 }  // namespace
 
-template <class T, int D, int G>
-__global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeParams p) {
+template <class T, int D, int G, int NW>
+__global__ __launch_bounds__(NW *kWave) void decode_split_kernel(DecodeParams p) {
     using S = typename T::storage;
     constexpr int KS = D / 32;  // 32-wide contraction slices over the head dim
     constexpr int CH = D / 16;  // head-dim elements per lane in the value operand
     static_assert(2 * G <= 16, "query + probe rows must fit 16 MFMA columns");
 
-    const int lane = threadIdx.x;
+    // Wavefronts of the workgroup take interleaved 32-key tiles of the chunk
+    // and merge their softmax states through LDS at the end.
+    __shared__ float s_m[NW > 1 ? NW : 1][16];
+    __shared__ float s_l[NW > 1 ? NW : 1][16];
+    __shared__ __attribute__((aligned(16))) float s_acc[NW > 1 ? NW : 1][CH * 4][kWave];
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int64_t item = blockIdx.x;
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeParams p) {
     if (k_begin >= sv.len) {
         // Nothing to read.  With a single split this kernel also owns the
         // output, and an empty sequence returns zeros.
-        if (p.n_split == 1) {
+        if (p.n_split == 1 && wave == 0) {
             S *o = static_cast<S *>(p.out) + (static_cast<int64_t>(b) * p.Hq + g * G) * D;
             for (int e = lane; e < G * D; e += kWave) o[e] = to_storage(0.f, T{});
         }
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int t = 0; t < CH; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kt = k_begin; kt < k_end; kt += 32) {
+    for (int64_t kt = k_begin + 32 * wave; kt < k_end; kt += 32 * NW) {
         // K: A operand rows are keys kt + 16*blk + col (clamped into the chunk;
         // clamped keys are masked below).
         Op8<T> kop[2][KS];
@@ -240,6 +247,42 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeParams p) {
     }
 
     rsum = group_sum(rsum);
+
+    if constexpr (NW > 1) {
+        // Probe columns are weighted by the max of their query column.  The
+        // lane shift runs on every lane (its source lanes must be active).
+        const float m_q = row_shr<G>(m_run);
+        const float m_eff = is_r ? m_q : m_run;
+        if (grp == 0) {
+            s_m[wave][col] = m_eff;
+            s_l[wave][col] = rsum;
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_acc[wave][4 * t + i][lane] = acc[t][i];
+        __syncthreads();
+        if (wave != 0) return;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][col]);
+        rsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            // A wavefront that saw no keys has m = -inf and weight 0.
+            const float wt = fast_exp2(s_m[w][col] - M);
+            rsum += wt * s_l[w][col];
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][i] += wt * s_acc[w][4 * t + i][lane];
+        }
+        // Only the query columns' m is read below (partials); probe columns
+        // carry the query column's weights already.
+        m_run = M;
+    }
 
     // acc[t][i] of this lane is head-dim CH*(4*grp + i) + t of its column.
     if (p.n_split == 1) {
@@ -341,11 +384,20 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
 
 namespace {
 
+// Wavefronts per workgroup: one per 128 keys of the chunk, at most 8.
+template <class T, int D, int G, int NW>
+void launch_split(const DecodeParams &p, int64_t items, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, NW>), dim3(static_cast<uint32_t>(items)), dim3(NW * kWave), 0,
+                       stream, p);
+}
+
 template <class T, int D, int G>
 hipError_t launch_decode_g(const DecodeParams &p, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(p.B) * p.Hkv * p.n_split;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<uint32_t>(items)), dim3(kWave), 0,
-                       stream, p);
+    if (p.keys_per_split >= 1024) launch_split<T, D, G, 8>(p, items, stream);
+    else if (p.keys_per_split >= 512) launch_split<T, D, G, 4>(p, items, stream);
+    else if (p.keys_per_split >= 256) launch_split<T, D, G, 2>(p, items, stream);
+    else launch_split<T, D, G, 1>(p, items, stream);
     if (p.n_split > 1) {
         const int64_t rows = static_cast<int64_t>(p.B) * p.Hq;
         hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(static_cast<uint32_t>(rows)), dim3(kWave), 0,

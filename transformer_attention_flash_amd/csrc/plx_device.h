@@ -140,7 +140,8 @@ __device__ __forceinline__ uint32_t half_lo(uint32_t w, int e) { return (e & 1) 
 __device__ __forceinline__ uint32_t half_hi(uint32_t w, int e) { return (e & 1) ? (w & 0xffff0000u) : (w << 16); }
 
 // Value of lane (l - SH) within the same 16-lane row (DPP row_shr); lanes
-// with no source get 0.
+// with no source get 0.  Call it where every lane is active: a source lane
+// that is switched off also yields 0.
 template <int SH>
 __device__ __forceinline__ float row_shr(float x) {
     static_assert(SH >= 1 && SH <= 15, "row_shr distance");
