@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NW *kWave) void decode_split_kernel(DecodeParams p)
         }
         const float alpha = is_q ? alpha_own : (is_r ? alpha_q : 1.f);
         const Op8<T> pop = op8_pack(pv, T{});
-        rsum = alpha * rsum + op8_sum(pop);
+        rsum = op8_sum_acc(pop, alpha * rsum);
 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {

@@ -115,25 +115,32 @@ __device__ __forceinline__ Op8<F32> op8_pack(const float (&x)[8], F32) {
     return o;
 }
 
-// Sum of the 8 operand values exactly as the MFMA sees them (after rounding to
-// bf16).  Row sums taken over these values make the weights that multiply V
-// sum exactly to the normaliser, so rounding perturbs the weights but not
-// their total.
-__device__ __forceinline__ float op8_sum(const Op8<BF16> &o) {
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        s += __builtin_bit_cast(float, o.w[j] << 16);
-        s += __builtin_bit_cast(float, o.w[j] & 0xffff0000u);
-    }
-    return s;
+// acc + the sum of the 8 operand values exactly as the MFMA sees them (after
+// rounding to bf16).  Row sums taken over these values make the weights that
+// multiply V sum exactly to the normaliser, so rounding perturbs the weights
+// but not their total.  For bf16 each pair is one v_dot2 against (1, 1).
+__device__ __forceinline__ float op8_sum_acc(const Op8<BF16> &o, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    // Words are copied to scalars first: a bit_cast straight from a vector
+    // element (o.w[j]) compiled to a read of element 0 for every j.
+    const uint32_t w0 = o.w.x, w1 = o.w.y, w2 = o.w.z, w3 = o.w.w;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), one, acc, false);
+    return acc;
 }
-__device__ __forceinline__ float op8_sum(const Op8<F32> &o) {
-    float s = 0.f;
+__device__ __forceinline__ float op8_sum_acc(const Op8<F32> &o, float acc) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += o.v[e];
-    return s;
+    for (int e = 0; e < 8; ++e) acc += o.v[e];
+    return acc;
 }
+template <class T>
+__device__ __forceinline__ float op8_sum(const Op8<T> &o) { return op8_sum_acc(o, 0.f); }
+
+// Wave-uniform "any lane": true on every lane if pred holds on one.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 // 16-bit element `e` of a packed bf16 pair word, as the low or high half.
 __device__ __forceinline__ uint32_t half_lo(uint32_t w, int e) { return (e & 1) ? (w >> 16) : (w & 0xffffu); }

@@ -46,6 +46,7 @@ template <> struct PrefillCfg<F32> {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kColTiles = 2;  // 16-row column tiles per wavefront
+constexpr float kRescaleSlack = 8.f;
 
 // Four Op8 rows (keys 4r .. 4r+3 of one 8-dim chunk) -> element e of each, as
 // the 4 contiguous LDS entries of transposed row e.
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
         for (int n = 0; n < NVR; ++n) {
             const int it = tid + n * NTHR;
             if (it < VRUN) {
-                const int chunk = it % (D / 8);
-                const int run = it / (D / 8);
+                const int run = it % (KT / 4);
+                const int chunk = it / (KT / 4);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int kk = min(key0 + 4 * run + i, T_len - 1);
@@ -189,8 +190,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
         for (int n = 0; n < NVR; ++n) {
             const int it = tid + n * NTHR;
             if (it < VRUN) {
-                const int chunk = it % (D / 8);
-                const int run = it / (D / 8);
+                // Consecutive threads take consecutive 4-key runs of one 8-dim
+                // chunk, so a store instruction writes one transposed row.
+                const int run = it % (KT / 4);
+                const int chunk = it / (KT / 4);
                 const int blk = run >> 2, q = run & 3;
                 const int vpos = 32 * (blk >> 1) + 8 * q + 4 * (blk & 1);
 #pragma unroll
@@ -255,48 +258,55 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
             Op8<T> prop[NB][HAS_RHO ? NU : 1];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
+                // Raw scores; the scale is folded into the exponent below.
                 float x[NKB * 4];
                 float mt = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < NKB * 4; ++e) {
                     const int key = key0 + 16 * (e >> 2) + 4 * grp + (e & 3);
-                    float v = sacc[nb][e >> 2][e & 3] * p.scale_log2;
+                    float v = sacc[nb][e >> 2][e & 3];
                     if (diag && key > pos[nb]) v = -INFINITY;
                     x[e] = v;
                     mt = fmaxf(mt, v);
                 }
-                mt = group_max(mt);
-                const float m_new = fmaxf(m_run[nb], mt);
-                const float alpha = fast_exp2(m_run[nb] - m_new);
-                m_run[nb] = m_new;
+                mt = group_max(mt) * p.scale_log2;
+                // The running max only moves when some row's max grows by more
+                // than kRescaleSlack (log2 units), so P stays below 2^slack and
+                // the rescale of l, c, A, B is rare; the decision is
+                // wave-uniform.
+                if (wave_any(mt > m_run[nb] + kRescaleSlack)) {
+                    const float m_new = fmaxf(m_run[nb], mt);
+                    const float alpha = fast_exp2(m_run[nb] - m_new);
+                    m_run[nb] = m_new;
+                    lsum[nb] *= alpha;
+                    if constexpr (HAS_RHO) csum[nb] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < DT; ++t) {
+                        acc_a[nb][t] *= alpha;
+                        if constexpr (HAS_RHO) acc_b[nb][t] *= alpha;
+                    }
+                }
+                const float neg_m = -m_run[nb];
                 float pr[NKB * 4];
 #pragma unroll
                 for (int e = 0; e < NKB * 4; ++e) {
-                    x[e] = fast_exp2(x[e] - m_new);
+                    x[e] = fast_exp2(fmaf(x[e], p.scale_log2, neg_m));
                     if constexpr (HAS_RHO) pr[e] = x[e] * racc[nb][e >> 2][e & 3];
                 }
-                // Row sums over the rounded operands (see op8_sum).
-                float ps = 0.f, cs = 0.f;
+                // Row sums over the rounded operands (see op8_sum_acc).
 #pragma unroll
                 for (int u = 0; u < NU; ++u) {
                     float w[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) w[e] = x[8 * u + e];
                     pop[nb][u] = op8_pack(w, T{});
-                    ps += op8_sum(pop[nb][u]);
+                    lsum[nb] = op8_sum_acc(pop[nb][u], lsum[nb]);
                     if constexpr (HAS_RHO) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) w[e] = pr[8 * u + e];
                         prop[nb][u] = op8_pack(w, T{});
-                        cs += op8_sum(prop[nb][u]);
+                        csum[nb] = op8_sum_acc(prop[nb][u], csum[nb]);
                     }
-                }
-                lsum[nb] = alpha * lsum[nb] + ps;
-                if constexpr (HAS_RHO) csum[nb] = alpha * csum[nb] + cs;
-#pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    acc_a[nb][t] *= alpha;
-                    if constexpr (HAS_RHO) acc_b[nb][t] *= alpha;
                 }
             }
 
