@@ -44,8 +44,8 @@ template <> struct PrefillCfg<F32> {
     static constexpr int KT = 32;
 };
 
-constexpr int kPrefillWaves = 4;
-constexpr int kColTiles = 2;  // 16-row column tiles per wavefront
+constexpr int kPrefillWaves = 8;
+constexpr int kColTiles = 1;  // 16-row column tiles per wavefront
 constexpr float kRescaleSlack = 8.f;
 
 // Four Op8 rows (keys 4r .. 4r+3 of one 8-dim chunk) -> element e of each, as
