@@ -96,9 +96,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
 }
 
+// Two fp32 -> one packed bf16 pair (lo in bits 0..15) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-    return static_cast<uint32_t>(to_storage(lo, BF16{})) |
-           (static_cast<uint32_t>(to_storage(hi, BF16{})) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // Eight fp32 values -> a B operand (probabilities, probe-weighted probabilities).

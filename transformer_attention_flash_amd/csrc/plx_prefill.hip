@@ -260,15 +260,17 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
             for (int nb = 0; nb < NB; ++nb) {
                 // Raw scores; the scale is folded into the exponent below.
                 float x[NKB * 4];
+#pragma unroll
+                for (int e = 0; e < NKB * 4; ++e) x[e] = sacc[nb][e >> 2][e & 3];
+                if (diag) {  // wave-uniform: only tiles that cross the diagonal
+                    const int rel = pos[nb] - key0 - 4 * grp;  // key > pos <=> offset > rel
+#pragma unroll
+                    for (int e = 0; e < NKB * 4; ++e)
+                        if (16 * (e >> 2) + (e & 3) > rel) x[e] = -INFINITY;
+                }
                 float mt = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < NKB * 4; ++e) {
-                    const int key = key0 + 16 * (e >> 2) + 4 * grp + (e & 3);
-                    float v = sacc[nb][e >> 2][e & 3];
-                    if (diag && key > pos[nb]) v = -INFINITY;
-                    x[e] = v;
-                    mt = fmaxf(mt, v);
-                }
+                for (int e = 0; e < NKB * 4; ++e) mt = fmaxf(mt, x[e]);
                 mt = group_max(mt) * p.scale_log2;
                 // The running max only moves when some row's max grows by more
                 // than kRescaleSlack (log2 units), so P stays below 2^slack and
