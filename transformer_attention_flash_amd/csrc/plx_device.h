@@ -73,6 +73,22 @@ __device__ __forceinline__ Op8<F32> op8_load(const float *p) {
     return o;
 }
 
+// Value operand from two transposing LDS reads (ds_read_b64_tr_b16).  Within
+// each 16-lane group, lane j receives element j % 4 of the 8-byte rows that
+// lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12 point at, in that order; `lo`
+// supplies operand elements 0..3 and `hi` elements 4..7.
+__device__ __forceinline__ Op8<BF16> op8_load_tr(const uint16_t *lo, const uint16_t *hi) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lo));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(hi));
+    const u32x2 wa = __builtin_bit_cast(u32x2, a);
+    const u32x2 wb = __builtin_bit_cast(u32x2, b);
+    Op8<BF16> o;
+    o.w = u32x4{wa.x, wa.y, wb.x, wb.y};
+    return o;
+}
+
 // C += A * B over one 32-wide contraction slice.
 __device__ __forceinline__ f32x4 mma32(const Op8<BF16> &a, const Op8<BF16> &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.w),

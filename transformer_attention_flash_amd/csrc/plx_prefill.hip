@@ -20,15 +20,20 @@
 //
 // LDS layouts:
 //   K  [KT][D + pad]  natural rows; a lane's A operand is 8 contiguous dims.
-//   Vt [D][KT + pad]  transposed, with the keys of each 32-key slice permuted
-//                     so that the 8 keys a lane needs for one value operand
-//                     are contiguous: key 16*blk + 4*q + i (blk = 16-key block
-//                     of the score tile, q = lane group, i = C-tile row) sits
-//                     at position 32*(blk/2) + 8*q + 4*(blk%2) + i.  The
+//   V (bf16) [KT][D + pad] natural rows, read with the gfx950 transposing LDS
+//                     load ds_read_b64_tr_b16: two of them give a lane the 8
+//                     keys of one head dimension that a value operand needs.
+//   Vt (fp32) [D][KT + pad] transposed, with the keys of each 32-key slice
+//                     permuted so that the 8 keys a lane needs for one value
+//                     operand are contiguous: key 16*blk + 4*q + i (blk = 16-key
+//                     block of the score tile, q = lane group, i = C-tile row)
+//                     sits at position 32*(blk/2) + 8*q + 4*(blk%2) + i.  The
 //                     loader transposes 4-key x 8-dim blocks in registers.
 // The softmax-only kernel (no probe) is the same template with the probe
 // branch compiled out; it runs the query-side arithmetic in the same order,
 // so a zero probe reproduces its output bit for bit.
+#include <type_traits>
+
 #include "plx_device.h"
 #include "plx_kernels.h"
 
@@ -77,7 +82,7 @@ __device__ __forceinline__ void store4(float *dst, const float (&y)[4]) {
 }  // namespace
 
 template <class T, int D, int G, bool HAS_RHO>
-__global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(PrefillParams p) {
     using S = typename T::storage;
     constexpr int KT = PrefillCfg<T>::KT;
     constexpr int NB = kColTiles;
@@ -89,7 +94,12 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
     constexpr int DT = D / 16;               // 16-dim output tiles
     constexpr int PAD = 16 / sizeof(S);      // one 16-byte bank group of padding
     constexpr int KRS = D + PAD;             // K row stride (elements)
-    constexpr int VRS = KT + PAD;            // Vt row stride (elements)
+    constexpr int VRS = KT + PAD;            // Vt row stride (elements), transposed layout
+    // bf16 V stays in natural [key][dim] rows and is read transposed by
+    // ds_read_b64_tr_b16; 16 extra elements per row put the 4 key rows one
+    // transposed read touches in distinct banks.
+    constexpr bool VNAT = std::is_same<T, BF16>::value;
+    constexpr int VNRS = D + 16;             // V row stride (elements), natural layout
     constexpr int NTHR = kPrefillWaves * kWave;
     constexpr int KCH = KT * D / 8;          // 8-element K chunks per tile
     constexpr int NKC = (KCH + NTHR - 1) / NTHR;
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
     static_assert(16 * NB % G == 0, "group size must divide the wave's rows");
 
     __shared__ __attribute__((aligned(16))) S lds_k[2][KT * KRS];
-    __shared__ __attribute__((aligned(16))) S lds_v[2][D * VRS];
+    __shared__ __attribute__((aligned(16))) S lds_v[2][VNAT ? KT * VNRS : D * VRS];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -149,7 +159,8 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
 
     // Loader registers for one tile.
     Op8<T> kreg[NKC];
-    Op8<T> vreg[NVR][4];
+    Op8<T> vnreg[VNAT ? NKC : 1];
+    Op8<T> vreg[VNAT ? 1 : NVR][4];
     auto load_tile = [&](int j) {
         const int key0 = j * KT;
 #pragma unroll
@@ -160,8 +171,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
                 const int off = (c % (D / 8)) * 8;
                 const int kk = min(key0 + key, T_len - 1);
                 kreg[n] = op8_load(kg + static_cast<int64_t>(kk) * D + off);
+                if constexpr (VNAT) vnreg[n] = op8_load(vg + static_cast<int64_t>(kk) * D + off);
             }
         }
+        if constexpr (VNAT) return;
 #pragma unroll
         for (int n = 0; n < NVR; ++n) {
             const int it = tid + n * NTHR;
@@ -184,8 +197,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
                 const int key = c / (D / 8);
                 const int off = (c % (D / 8)) * 8;
                 store_op8(&lds_k[buf][key * KRS + off], kreg[n]);
+                if constexpr (VNAT) store_op8(&lds_v[buf][key * VNRS + off], vnreg[n]);
             }
         }
+        if constexpr (VNAT) return;
 #pragma unroll
         for (int n = 0; n < NVR; ++n) {
             const int it = tid + n * NTHR;
@@ -316,7 +331,18 @@ __global__ __launch_bounds__(kPrefillWaves *kWave) void prefill_kernel(PrefillPa
             for (int u = 0; u < NU; ++u) {
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
-                    const Op8<T> vop = op8_load(vt + (16 * t + col) * VRS + 32 * u + 8 * grp);
+                    Op8<T> vop;
+                    if constexpr (VNAT) {
+                        // Lane col of group grp names key 32u + 4grp + col/4 (and
+                        // that key + 16) at dims 16t + 4(col%4) .. +3; the transposed
+                        // read returns to lane col dim 16t + col of the 4 keys named
+                        // by lanes col/4, col/4 + 4, col/4 + 8, col/4 + 12, i.e. keys
+                        // 32u + 4grp + 0..3: the k-slots of this lane group.
+                        const S *a = vt + (32 * u + 4 * grp + (col >> 2)) * VNRS + 16 * t + 4 * (col & 3);
+                        vop = op8_load_tr(a, a + 16 * VNRS);
+                    } else {
+                        vop = op8_load(vt + (16 * t + col) * VRS + 32 * u + 8 * grp);
+                    }
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         acc_a[nb][t] = mma32(vop, pop[nb][u], acc_a[nb][t]);
