@@ -19,7 +19,7 @@
 // state is computed once.  The epilogue forms o = A/l - (B/l - (c/l) A/l).
 //
 // LDS layouts:
-//   K  [KT][D + pad]  natural rows; a lane's A operand is 8 contiguous dims.
+//   K  [KT][D + 32 B] natural rows; a lane's A operand is 8 contiguous dims.
 //   V (bf16) [KT][D + pad] natural rows, read with the gfx950 transposing LDS
 //                     load ds_read_b64_tr_b16: two of them give a lane the 8
 //                     keys of one head dimension that a value operand needs.
@@ -93,7 +93,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     constexpr int NU = KT / 32;              // 32-key slices for the value GEMMs
     constexpr int DT = D / 16;               // 16-dim output tiles
     constexpr int PAD = 16 / sizeof(S);      // one 16-byte bank group of padding
-    constexpr int KRS = D + PAD;             // K row stride (elements)
+    // K rows carry 32 bytes of padding: with 16 the 16-byte operand reads of
+    // consecutive key rows hit the same banks in pairs (measured); with 32
+    // they are conflict-free and so are the tile stores.
+    constexpr int KRS = D + 32 / sizeof(S);  // K row stride (elements)
     constexpr int VRS = KT + PAD;            // Vt row stride (elements), transposed layout
     // bf16 V stays in natural [key][dim] rows and is read transposed by
     // ds_read_b64_tr_b16; 16 extra elements per row put the 4 key rows one
@@ -286,12 +289,14 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 float mt = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < NKB * 4; ++e) mt = fmaxf(mt, x[e]);
-                mt = group_max(mt) * p.scale_log2;
+                mt *= p.scale_log2;  // this lane's max; the row max needs 4 lanes
                 // The running max only moves when some row's max grows by more
                 // than kRescaleSlack (log2 units), so P stays below 2^slack and
-                // the rescale of l, c, A, B is rare; the decision is
-                // wave-uniform.
+                // the rescale of l, c, A, B is rare.  Testing each lane's own
+                // max is enough to decide (wave-uniformly); the cross-lane row
+                // max is only formed when a rescale happens.
                 if (wave_any(mt > m_run[nb] + kRescaleSlack)) {
+                    mt = group_max(mt);
                     const float m_new = fmaxf(m_run[nb], mt);
                     const float alpha = fast_exp2(m_run[nb] - m_new);
                     m_run[nb] = m_new;
