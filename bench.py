@@ -145,8 +145,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,11 +256,11 @@ def main():
             x = psets[i % len(psets)]
             plx.prefill(x["q"], x["k"], x["v"], None, out=pout)
 
-        psecs, pper = time_steps(prefill_step, args.prefill_steps, 2, torch)
+        psecs, pper = time_steps(prefill_step, args.prefill_steps, args.prefill_warmup, torch)
         pairs = pw.B * pw.Hq * pw.T * (pw.T + 1) // 2
         pflops = 4 * 2 * pw.d * pairs
         tf = pflops / (psecs / args.prefill_steps) / 1e12
-        ssecs, _ = time_steps(softmax_only_step, args.prefill_steps, 2, torch)
+        ssecs, _ = time_steps(softmax_only_step, args.prefill_steps, args.prefill_warmup, torch)
         stf = 2 * 2 * pw.d * pairs / (ssecs / args.prefill_steps) / 1e12
         log(f"prefill: {psecs / args.prefill_steps * 1e3:.3f} ms/step, {tf:.1f} TFLOP/s; softmax-only "
             f"{ssecs / args.prefill_steps * 1e3:.3f} ms, {stf:.1f} TFLOP/s")
