@@ -52,6 +52,7 @@ template <> struct PrefillCfg<F32> {
 constexpr int kPrefillWaves = 8;
 constexpr int kColTiles = 1;  // 16-row column tiles per wavefront
 constexpr float kRescaleSlack = 8.f;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 // Four Op8 rows (keys 4r .. 4r+3 of one 8-dim chunk) -> element e of each, as
 // the 4 contiguous LDS entries of transposed row e.
@@ -119,11 +120,23 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    // Longest query blocks first: they have the most key tiles.
+    // Workgroups are dealt to the 8 XCDs round-robin by id, and each XCD has
+    // its own 4 MB L2.  When the (b, kv head) units divide evenly, XCD x runs
+    // units x, x + 8, ... one after another, each with its query blocks
+    // longest first: the CUs of an XCD then stream the same unit's K/V
+    // (2 MB at T = 4096, d = 128) together, so it is fetched into L2 about
+    // once instead of once per query block.
     const int n_units = p.B * p.Hkv;
     const int id = blockIdx.x;
-    const int qb = p.n_qblk - 1 - id / n_units;
-    const int unit = id % n_units;
+    int qb, unit;
+    if (n_units % kXcds == 0) {
+        const int xcd = id % kXcds, slot = id / kXcds;
+        qb = p.n_qblk - 1 - slot % p.n_qblk;
+        unit = xcd + kXcds * (slot / p.n_qblk);
+    } else {  // longest query blocks first
+        qb = p.n_qblk - 1 - id / n_units;
+        unit = id % n_units;
+    }
     const int b = unit / p.Hkv;
     const int g = unit % p.Hkv;
     const int T_len = p.T;
@@ -252,6 +265,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
 
             f32x4 sacc[NB][NKB];
             f32x4 racc[NB][HAS_RHO ? NKB : 1];
+            // Matrix phases run at raised wave priority so that a wavefront
+            // issuing MFMAs gets the issue slots while its SIMD partner is in
+            // the VALU-heavy softmax.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 Op8<T> kop[KS];
@@ -272,6 +289,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 }
             }
 
+            __builtin_amdgcn_s_setprio(0);
             Op8<T> pop[NB][NU];
             Op8<T> prop[NB][HAS_RHO ? NU : 1];
 #pragma unroll
@@ -332,6 +350,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 }
             }
 
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
 #pragma unroll
@@ -357,6 +376,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
             }
         }
 
+        __builtin_amdgcn_s_setprio(0);
         if (more) store_tile(buf ^ 1);
     }
 
