@@ -177,17 +177,39 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     Op8<T> kreg[NKC];
     Op8<T> vnreg[VNAT ? NKC : 1];
     Op8<T> vreg[VNAT ? 1 : NVR][4];
+    // This thread's 8-element chunks of a K (and bf16 V) tile: element offset
+    // within the tile in global memory and in the two LDS layouts.
+    constexpr bool FULL = KCH % NTHR == 0;
+    int g_off[NKC], k_off[NKC], v_off[NKC];
+#pragma unroll
+    for (int n = 0; n < NKC; ++n) {
+        const int c = min(tid + n * NTHR, KCH - 1);
+        g_off[n] = (c / (D / 8)) * D + (c % (D / 8)) * 8;
+        k_off[n] = (c / (D / 8)) * KRS + (c % (D / 8)) * 8;
+        v_off[n] = (c / (D / 8)) * VNRS + (c % (D / 8)) * 8;
+    }
     auto load_tile = [&](int j) {
         const int key0 = j * KT;
+        if (key0 + KT <= T_len) {  // whole tile inside the sequence: no clamping
+            const S *kt = kg + static_cast<int64_t>(key0) * D;
+            const S *vt = vg + static_cast<int64_t>(key0) * D;
 #pragma unroll
-        for (int n = 0; n < NKC; ++n) {
-            const int c = tid + n * NTHR;
-            if (c < KCH) {
-                const int key = c / (D / 8);
-                const int off = (c % (D / 8)) * 8;
-                const int kk = min(key0 + key, T_len - 1);
-                kreg[n] = op8_load(kg + static_cast<int64_t>(kk) * D + off);
-                if constexpr (VNAT) vnreg[n] = op8_load(vg + static_cast<int64_t>(kk) * D + off);
+            for (int n = 0; n < NKC; ++n) {
+                if (FULL || tid + n * NTHR < KCH) {
+                    kreg[n] = op8_load(kt + g_off[n]);
+                    if constexpr (VNAT) vnreg[n] = op8_load(vt + g_off[n]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NKC; ++n) {
+                const int c = tid + n * NTHR;
+                if (FULL || c < KCH) {
+                    const int kk = min(key0 + c / (D / 8), T_len - 1);
+                    const int off = (c % (D / 8)) * 8;
+                    kreg[n] = op8_load(kg + static_cast<int64_t>(kk) * D + off);
+                    if constexpr (VNAT) vnreg[n] = op8_load(vg + static_cast<int64_t>(kk) * D + off);
+                }
             }
         }
         if constexpr (VNAT) return;
@@ -208,12 +230,9 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int n = 0; n < NKC; ++n) {
-            const int c = tid + n * NTHR;
-            if (c < KCH) {
-                const int key = c / (D / 8);
-                const int off = (c % (D / 8)) * 8;
-                store_op8(&lds_k[buf][key * KRS + off], kreg[n]);
-                if constexpr (VNAT) store_op8(&lds_v[buf][key * VNRS + off], vnreg[n]);
+            if (FULL || tid + n * NTHR < KCH) {
+                store_op8(&lds_k[buf][k_off[n]], kreg[n]);
+                if constexpr (VNAT) store_op8(&lds_v[buf][v_off[n]], vnreg[n]);
             }
         }
         if constexpr (VNAT) return;
