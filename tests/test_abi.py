@@ -111,12 +111,16 @@ def test_decode_workspace_size(lib):
 
 def test_decode_auto_split(lib):
     f = lib.parallax_fwd_decode_auto_split
-    assert f(2048, 16, 8, 128, 128) == 128          # one chunk, no merge
+    assert f(2048, 16, 8, 128, 128) == 256          # one chunk, no merge
     assert f(2, 16, 8, 128, 200) == 256
     assert f(64, 16, 8, 128, 4096) == 4096          # one chunk per (b, g): no merge kernel
-    assert f(1, 16, 8, 128, 4096) == 512            # few sequences: more, smaller chunks
-    assert f(256, 16, 8, 128, 32768) == 4096
-    assert f(2048, 32, 16, 64, 32768) == 4096
+    assert f(256, 16, 8, 128, 32768) == 32768
+    assert f(2048, 32, 16, 64, 32768) == 32768
+    assert f(2048, 32, 16, 64, 30000) == 32768      # rounded up to a power of two
+    assert f(1, 16, 8, 128, 4096) == 256            # few sequences: more, smaller chunks
+    assert f(8, 16, 8, 128, 65536) == 8192          # 64 (b, g) units x 8 chunks = 512 workgroups
+    assert f(1, 8, 8, 128, 1 << 24) == 1 << 18      # 8 units x 64 chunks = 512 workgroups
+    assert f(64, 8, 8, 128, 1 << 24) == 1 << 20     # chunk capped at 2^20 keys
     assert f(2, 6, 4, 128, 100) == -INVALID
     assert f(2, 4, 2, 100, 100) == -UNSUP
 

@@ -39,18 +39,19 @@ plx_status_t check_heads(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, float sc
 
 // Keys per chunk when the caller leaves it to the library.  A chunk is one
 // workgroup of up to 8 wavefronts (one per 128 keys) that merge their states
-// in LDS, so large chunks are cheap; chunks stay as large as possible
-// (up to 4096 keys, which needs no merge kernel for contexts up to 4096)
-// while keeping at least 512 workgroups (2 per CU) in flight.  Contexts of
-// up to 256 keys stay in one chunk.
+// in LDS, so large chunks are cheap.  Chunks are as large as possible -- one
+// per sequence, so no merge kernel runs -- unless that launches fewer than
+// 512 workgroups (2 per CU), in which case they are halved until it does or
+// reach 256 keys.  Measured on the decode workloads: one chunk per sequence
+// is best for 4096 keys x 64 sequences and for a ragged batch of 2048
+// sequences (8 chunks per sequence there cost 1.5x), and within 1% for 256
+// sequences of 32768 keys.  Contexts of up to 256 keys use one 256-key chunk
+// (two wavefronts), which measured faster than one wavefront at 128 keys.
 int32_t auto_keys_per_split(int64_t units, int64_t max_ctx) {
-    if (max_ctx <= 256) {  // one chunk, rounded up to a power of two
-        int32_t ks = 32;
-        while (ks < max_ctx) ks *= 2;
-        return ks;
-    }
-    int32_t ks = 4096;
-    while (ks > 512 && units * ((max_ctx + ks - 1) / ks) < 512) ks /= 2;
+    if (max_ctx <= 256) return 256;
+    int32_t ks = 256;
+    while (ks < max_ctx && ks < kMaxKeysPerSplit) ks *= 2;
+    while (ks > 256 && units * ((max_ctx + ks - 1) / ks) < 512) ks /= 2;
     return ks;
 }
 

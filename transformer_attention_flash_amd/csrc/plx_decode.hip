@@ -32,6 +32,8 @@ namespace plx {
 
 namespace {
 
+constexpr float kRescaleSlack = 8.f;
+
 // The d/16 head-dimension elements a lane reads from one value row.
 template <class T, int CH> struct VChunk;
 template <int CH> struct VChunk<BF16, CH> {
@@ -180,69 +182,91 @@ __global__ __launch_bounds__(NW *kWave) void decode_split_kernel(DecodeParams p)
 #pragma unroll
     for (int t = 0; t < CH; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kt = k_begin + 32 * wave; kt < k_end; kt += 32 * NW) {
+    // Each iteration covers SUB 32-key sub-tiles whose loads are all issued
+    // before any is used, so a wavefront keeps 16 KB of K/V in flight at
+    // either head dimension (d = 64 rows are half as long).
+    constexpr int SUB = D == 64 ? 2 : 1;
+    for (int64_t kt0 = k_begin + 32 * SUB * wave; kt0 < k_end; kt0 += 32 * SUB * NW) {
         // K: A operand rows are keys kt + 16*blk + col (clamped into the chunk;
         // clamped keys are masked below).
-        Op8<T> kop[2][KS];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int64_t key = min(kt + 16 * blk + col, last);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) kop[blk][s] = op8_load(kbase + key * D + 32 * s + 8 * grp);
-        }
+        Op8<T> kop[SUB][2][KS];
         // V: slot kk of this lane is key kt + 16*(kk/4) + 4*grp + kk%4, the
         // same key the score tile hands this lane in C position (kk/4, kk%4).
-        VChunk<T, CH> vr[8];
+        VChunk<T, CH> vr[SUB][8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int64_t key = min(kt + 16 * (kk >> 2) + 4 * grp + (kk & 3), last);
-            vr[kk] = vchunk_load<CH>(vbase + key * D + CH * col);
+        for (int sb = 0; sb < SUB; ++sb) {
+            const int64_t kt = kt0 + 32 * sb;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int64_t key = min(kt + 16 * blk + col, last);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) kop[sb][blk][s] = op8_load(kbase + key * D + 32 * s + 8 * grp);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const int64_t key = min(kt + 16 * (kk >> 2) + 4 * grp + (kk & 3), last);
+                vr[sb][kk] = vchunk_load<CH>(vbase + key * D + CH * col);
+            }
         }
 
-        // [S; R]^T for 32 keys.
-        f32x4 sr[2];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sr[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb < SUB; ++sb) {
+            const int64_t kt = kt0 + 32 * sb;
+            // [S; R]^T for 32 keys.
+            f32x4 sr[2];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) sr[blk] = mma32(kop[blk][s], qop[s], sr[blk]);
-        }
+            for (int blk = 0; blk < 2; ++blk) {
+                sr[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) sr[blk] = mma32(kop[sb][blk][s], qop[s], sr[blk]);
+            }
 
-        float x[8];
-        float mt = -INFINITY;
+            float x[8];
+            float mt = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t key = kt + 16 * (e >> 2) + 4 * grp + (e & 3);
-            float v = sr[e >> 2][e & 3] * sc;
-            if (is_q && key > last) v = -INFINITY;
-            x[e] = v;
-            mt = fmaxf(mt, v);
-        }
-        mt = group_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha_own = fast_exp2(m_run - m_new);
-        m_run = m_new;
+            for (int e = 0; e < 8; ++e) {
+                const int64_t key = kt + 16 * (e >> 2) + 4 * grp + (e & 3);
+                float v = sr[e >> 2][e & 3] * sc;
+                if (is_q && key > last) v = -INFINITY;
+                x[e] = v;
+                mt = fmaxf(mt, v);
+            }
+            // The running max only moves when some query column's tile max
+            // exceeds it by more than kRescaleSlack (log2 units): P stays below
+            // 2^slack, and the rescale of l, c, A, B is rare.  The decision is
+            // wave-uniform; the cross-lane row max is only formed when it fires.
+            const bool grow = wave_any(is_q && mt > m_run + kRescaleSlack);
+            float alpha_own = 1.f;
+            if (grow) {
+                mt = group_max(mt);
+                const float m_new = fmaxf(m_run, mt);
+                alpha_own = fast_exp2(m_run - m_new);
+                m_run = m_new;
+            }
 
-        float pq[8];
+            float pq[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pq[e] = fast_exp2(x[e] - m_new);
-        // Probe columns take the probabilities and the rescale factor of the
-        // query column of the same head, G lanes to their left.
-        const float alpha_q = row_shr<G>(alpha_own);
-        float pv[8];
+            for (int e = 0; e < 8; ++e) pq[e] = fast_exp2(x[e] - m_run);
+            // Probe columns take the probabilities and the rescale factor of the
+            // query column of the same head, G lanes to their left.
+            const float alpha_q = row_shr<G>(alpha_own);
+            float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pf = row_shr<G>(pq[e]);
-            pv[e] = is_q ? pq[e] : (is_r ? pf * x[e] : 0.f);
-        }
-        const float alpha = is_q ? alpha_own : (is_r ? alpha_q : 1.f);
-        const Op8<T> pop = op8_pack(pv, T{});
-        rsum = op8_sum_acc(pop, alpha * rsum);
+            for (int e = 0; e < 8; ++e) {
+                const float pf = row_shr<G>(pq[e]);
+                pv[e] = is_q ? pq[e] : (is_r ? pf * x[e] : 0.f);
+            }
+            const float alpha = is_q ? alpha_own : (is_r ? alpha_q : 1.f);
+            const Op8<T> pop = op8_pack(pv, T{});
+            if (grow) {
+                rsum *= alpha;
+#pragma unroll
+                for (int t = 0; t < CH; ++t) acc[t] *= alpha;
+            }
+            rsum = op8_sum_acc(pop, rsum);
 
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            acc[t] *= alpha;
-            acc[t] = mma32(value_op<CH>(vr, t), pop, acc[t]);
+            for (int t = 0; t < CH; ++t) acc[t] = mma32(value_op<CH>(vr[sb], t), pop, acc[t]);
         }
     }
 
