@@ -141,6 +141,53 @@ def cpu_baseline_prefill(x, w, budget_s: float):
                       f"0..{w.T - 1}), fp64 expanded form, {spent:.1f} s"}
 
 
+def run_sweep(args, torch, plx, synth):
+    """Decode sweep, Parallax against the softmax-only path (rho = NULL) of the
+    same library: batch x context over the pages' range (batch 1..2048,
+    context 128..32768), Hq = 16, Hkv = 8, bf16.  Two settings:
+      I/O-matched:     Parallax and softmax-only at the same d = 128;
+      compute-matched: Parallax at d = 64 against softmax-only at d = 128
+                       (equal matrix flops per key: Parallax has two scoring
+                       and two value products, softmax attention one each).
+    Prints one JSON line per grid point."""
+    dev = "cuda"
+    grid = [(b, l) for b in (1, 16, 128, 1024, 2048) for l in (128, 1024, 8192, 32768) if b * l <= 1 << 23]
+
+    def timed(fn, nbytes):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        iters = max(5, min(200, int(3e-3 / max(nbytes / 6e12, 2e-6))))
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / iters * 1e3
+            best = t if best is None or t < best else best
+        return best
+
+    for B, L in grid:
+        row = {"B": B, "context": L}
+        for name, d, with_rho in (("parallax_d128", 128, True), ("softmax_d128", 128, False),
+                                  ("parallax_d64", 64, True)):
+            x = synth.make_decode(B, 16, 8, L, d, torch.bfloat16, dev, seed=0)
+            out = torch.empty_like(x["q"])
+            rho = x["rho"] if with_rho else None
+            nbytes = 4 * B * 8 * L * d
+            us = timed(lambda: plx.decode(x["q"], x["k"], x["v"], rho, out=out), nbytes)
+            row[name + "_us"] = round(us, 2)
+            row[name + "_GBs"] = round(nbytes / us / 1e3, 1)
+            del x, out
+        torch.cuda.empty_cache()
+        row["io_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d128_us"], 3)
+        row["compute_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d64_us"], 3)
+        print(json.dumps(row), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +199,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="decode sweep: Parallax vs softmax-only over batch x context (JSON lines)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -171,6 +220,10 @@ def main():
         sys.exit(1)
     plx.load_library()
     dev = "cuda"
+
+    if args.sweep:
+        run_sweep(args, torch, plx, synth)
+        return
 
     if args.copy_probe_mib:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters
