@@ -36,8 +36,11 @@ DECODE_WL = "decode_bf16_b64_hq16_hkv8_l4096_d128"
 PREFILL_WL = "prefill_bf16_b8_hq16_hkv8_t4096_d128"
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_traffic.md")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_b8_t4096_traffic.md")
 DECODE_SOURCES = ["transformer_attention_flash_amd/csrc/plx_decode.hip",
                   "transformer_attention_flash_amd/csrc/plx_device.h"]
+PREFILL_SOURCES = ["transformer_attention_flash_amd/csrc/plx_prefill.hip",
+                   "transformer_attention_flash_amd/csrc/plx_device.h"]
 
 
 def log(*a):
@@ -52,12 +55,12 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(digest: str):
-    """HBM bytes per decode launch from the committed counter summary, or
-    None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(digest: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch from a committed counter summary, or None when it
+    is missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
     f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -191,10 +194,12 @@ def run_sweep(args, torch, plx, synth):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=10)
+    # The clocks take a few dozen prefill calls (~50 ms of work) to settle
+    # after an idle spell; the warm-up covers that.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=60)
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,6 +315,7 @@ def main():
             plx.prefill(x["q"], x["k"], x["v"], None, out=pout)
 
         psecs, pper = time_steps(prefill_step, args.prefill_steps, args.prefill_warmup, torch)
+        ptraffic = read_traffic(source_digest(PREFILL_SOURCES), PREFILL_TRAFFIC_FILE)
         pairs = pw.B * pw.Hq * pw.T * (pw.T + 1) // 2
         pflops = 4 * 2 * pw.d * pairs
         tf = pflops / (psecs / args.prefill_steps) / 1e12
@@ -320,9 +326,14 @@ def main():
         result["prefill"] = {
             "workload": pw.name, "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_step": round(psecs / args.prefill_steps * 1e3, 4), "steps": args.prefill_steps,
+            "warmup": args.prefill_warmup,
+            "us_per_step_median": round(sorted(pper)[len(pper) // 2] * 1e3, 2),
+            "us_per_step_p10": round(sorted(pper)[len(pper) // 10] * 1e3, 2),
+            "us_per_step_p90": round(sorted(pper)[(9 * len(pper)) // 10] * 1e3, 2),
             "tokens_per_s": round(pw.B * pw.T / (psecs / args.prefill_steps), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None if ptraffic is None else round(ptraffic),
                          "kernel": "prefill_kernel<bf16, 128, 2, rho>",
                          "algorithmic_flops_per_launch": pflops},
             "softmax_only": {"value": round(stf, 2), "unit": "TFLOP/s",
