@@ -1,6 +1,6 @@
 /*
  * parallax.h -- C ABI of libparallax.so, the gfx950 (MI355X) forward pass of
- * Parallax attention.
+ * Parallax attention, and the causal-prefill backward pass.
  *
  * The operation.  For every query row i the library returns
  *
@@ -98,6 +98,87 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
                                   int32_t d, float softmax_scale,
                                   plx_dtype_t dtype, plx_stream_t stream);
+
+/*
+ * Causal prefill forward that also keeps what parallax_bwd_prefill needs
+ * (the training forward; the pages pretrain with this layer, news.chathome.org
+ * article, "Experiments").  Same inputs, output and conventions as
+ * parallax_fwd_prefill, bf16 only, plus:
+ *
+ *   out_sa : device, [B, Hq, T, d] bf16: the softmax-attention part o^SA =
+ *            A/l of each row.  Required with rho, must be NULL without it
+ *            (then o^SA is out itself).
+ *   lse    : device, [B, Hq, T] fp32: log2 of sum_j 2^(s_ij log2 e), with
+ *            s_ij = softmax_scale * q_i.k_j over the row's causal keys, so that
+ *            p_ij = 2^(s_ij log2 e - lse_i).
+ *   rbar   : device, [B, Hq, T] fp32: rbar_i = sum_j p_ij (rho_i . k_j).
+ *            Required with rho, must be NULL without it (then rbar = 0).
+ *
+ * Returns PLX_ERR_INVALID_ARGUMENT for a null lse, out_sa or rbar given
+ * without rho (or missing with it), or any output overlapping an input or
+ * another output; PLX_ERR_UNSUPPORTED for dtype != PLX_DTYPE_BF16; otherwise
+ * as parallax_fwd_prefill.
+ */
+plx_status_t parallax_fwd_prefill_train(const void *q, const void *k,
+                                        const void *v, const void *rho,
+                                        void *out, void *out_sa, float *lse,
+                                        float *rbar, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t T, int32_t d,
+                                        float softmax_scale, plx_dtype_t dtype,
+                                        plx_stream_t stream);
+
+/*
+ * Bytes of device workspace parallax_bwd_prefill needs: 16 bytes per query
+ * row, B * Hq * T * 16.  Returns SIZE_MAX for non-positive sizes.
+ */
+size_t parallax_bwd_prefill_workspace_size(int32_t B, int32_t Hq, int32_t T);
+
+/*
+ * Causal prefill backward: the gradients of sum(dout * o) with respect to
+ * q, k, v and rho, for the forward above.  The pages print no backward pass;
+ * writing the forward as o_i = sum_j w_ij v_j with
+ * w_ij = p_ij (1 - r_ij + rbar_i) and r_ij = rho_i . k_j, differentiation
+ * gives, with g_ij = dout_i . v_j, G_i = dout_i . o^SA_i and
+ * D_i = dout_i . o_i + rbar_i G_i:
+ *
+ *     dS_ij = p_ij (g_ij (1 - r_ij + rbar_i) + G_i r_ij - D_i)
+ *     dR_ij = p_ij (G_i - g_ij)
+ *     dq_i = tau sum_j dS_ij k_j          drho_i = sum_j dR_ij k_j
+ *     dk_j = tau sum_i dS_ij q_i + sum_i dR_ij rho_i
+ *     dv_j = sum_i w_ij dout_i
+ *
+ * (dk and dv of a KV head sum over its Hq / Hkv query heads).
+ *
+ *   q, k, v, rho : the forward's inputs (rho NULL: softmax-only backward)
+ *   out, out_sa, lse, rbar : the outputs of parallax_fwd_prefill_train
+ *                  (out_sa and rbar NULL exactly when rho is)
+ *   dout         : device, [B, Hq, T, d] bf16, upstream gradient
+ *   dq, drho     : device, [B, Hq, T, d] bf16 outputs (drho NULL exactly
+ *                  when rho is)
+ *   dk, dv       : device, [B, Hkv, T, d] bf16 outputs
+ *   workspace    : device, at least parallax_bwd_prefill_workspace_size
+ *                  bytes, 16-byte aligned; scratch, contents not kept
+ *
+ * Three kernels run on `stream`: per-row statistics into the workspace, then
+ * dq/drho, then dk/dv.  Every gradient is written in full (no accumulation
+ * into the outputs).  Accumulation is fp32; p, w, dS and dR are rounded to
+ * bf16 as matrix-core operands.
+ *
+ * Returns PLX_ERR_INVALID_ARGUMENT for null required pointers, a NULL pattern
+ * that does not match rho's, misaligned pointers, non-positive sizes, a bad
+ * scale, or an output overlapping an input, another output or the
+ * workspace; PLX_ERR_WORKSPACE_TOO_SMALL; PLX_ERR_UNSUPPORTED for
+ * dtype != PLX_DTYPE_BF16, other d or group sizes.
+ */
+plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v,
+                                  const void *rho, const void *out,
+                                  const void *out_sa, const float *lse,
+                                  const float *rbar, const void *dout,
+                                  void *dq, void *dk, void *dv, void *drho,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                  int32_t d, float softmax_scale,
+                                  plx_dtype_t dtype, void *workspace,
+                                  size_t workspace_bytes, plx_stream_t stream);
 
 /*
  * Bytes of device workspace parallax_fwd_decode needs for these sizes and

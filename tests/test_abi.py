@@ -18,7 +18,7 @@ SIZE_MAX = (1 << 64) - 1
 
 # Fake, never dereferenced device addresses: every call below is rejected by
 # the host checks before anything reaches the GPU.
-P = [0x10000000 * (i + 1) for i in range(8)]
+P = [0x10000000 * (i + 1) for i in range(16)]
 
 
 @pytest.fixture(scope="module")
@@ -70,6 +70,60 @@ def prefill(lib, q=P[0], k=P[1], v=P[2], rho=P[3], out=P[4], B=1, Hq=4, Hkv=2, T
 ])
 def test_prefill_rejections(lib, kw, code):
     assert prefill(lib, **kw) == code
+
+
+def prefill_train(lib, q=P[0], k=P[1], v=P[2], rho=P[3], out=P[4], out_sa=P[5], lse=P[6], rbar=P[7], B=1, Hq=4,
+                  Hkv=2, T=16, d=64, scale=0.125, dtype=BF16):
+    return lib.parallax_fwd_prefill_train(q, k, v, rho, out, out_sa, lse, rbar, B, Hq, Hkv, T, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), INVALID), (dict(rbar=None), INVALID), (dict(out_sa=None), INVALID),
+    (dict(rho=None), INVALID),                 # out_sa and rbar given without rho
+    (dict(rho=None, out_sa=None), INVALID),    # rbar given without rho
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(B=0), INVALID),
+    (dict(out_sa=P[4]), INVALID),              # out_sa aliases out
+    (dict(lse=P[0] + 256), INVALID),           # lse overlaps q
+    (dict(rbar=P[6] + 16), INVALID),           # rbar overlaps lse
+    (dict(lse=P[6] + 4), INVALID),             # alignment
+])
+def test_prefill_train_rejections(lib, kw, code):
+    assert prefill_train(lib, **kw) == code
+
+
+def backward(lib, q=P[0], k=P[1], v=P[2], rho=P[3], out=P[4], out_sa=P[5], lse=P[6], rbar=P[7], dout=P[8],
+             dq=P[9], dk=P[10], dv=P[11], drho=P[12], B=1, Hq=4, Hkv=2, T=16, d=64, scale=0.125, dtype=BF16,
+             ws=P[13], ws_bytes=1 << 20):
+    return lib.parallax_bwd_prefill(q, k, v, rho, out, out_sa, lse, rbar, dout, dq, dk, dv, drho, B, Hq, Hkv, T, d,
+                                    scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(dout=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
+    (dict(lse=None), INVALID), (dict(ws=None), INVALID),
+    (dict(drho=None), INVALID),                # rho given, drho missing
+    (dict(rho=None), INVALID),                 # drho/out_sa/rbar given without rho
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(scale=0.0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(d=32), UNSUP), (dict(Hq=48, Hkv=2), UNSUP),
+    (dict(ws_bytes=1023), WS),                 # needs 1 * 4 * 16 * 16 = 1024 bytes
+    (dict(dq=P[0]), INVALID),                  # dq aliases q
+    (dict(dv=P[10] + 32), INVALID),            # dv overlaps dk
+    (dict(dk=P[13]), INVALID),                 # dk overlaps the workspace
+    (dict(dq=P[9] + 8), INVALID), (dict(ws=P[13] + 4), INVALID),  # alignment
+])
+def test_backward_rejections(lib, kw, code):
+    assert backward(lib, **kw) == code
+
+
+def test_backward_rejects_partial_softmax_only(lib):
+    assert backward(lib, rho=None, out_sa=None, rbar=None) == INVALID      # drho without rho
+    assert backward(lib, rho=None, out_sa=None, drho=None) == INVALID      # rbar without rho
+
+
+def test_backward_workspace_size(lib):
+    assert lib.parallax_bwd_prefill_workspace_size(8, 16, 4096) == 8 * 16 * 4096 * 16
+    assert lib.parallax_bwd_prefill_workspace_size(0, 16, 4096) == SIZE_MAX
+    assert lib.parallax_bwd_prefill_workspace_size(1, 1, -1) == SIZE_MAX
 
 
 def decode(lib, q=P[0], rho=P[1], k=P[2], v=P[3], cu=None, max_ctx=4096, out=P[4], B=2, Hq=4, Hkv=2, d=128,

@@ -1,11 +1,13 @@
-"""Parallax attention forward on AMD MI355X (gfx950).
+"""Parallax attention on AMD MI355X (gfx950): forward (prefill, decode) and
+the causal-prefill backward.
 
 The computation lives in libparallax.so (hand-written HIP kernels behind the
 C ABI of include/parallax.h); this package binds it with ctypes and offers
 seeded synthetic inputs.  PyTorch supplies device memory and streams only.
 """
 from ._native import EXPORTS, LIB_PATH, ParallaxError, load as load_library
-from .api import decode, decode_auto_split, decode_workspace_size, prefill
+from .api import (ParallaxAttention, decode, decode_auto_split, decode_workspace_size, prefill,
+                  prefill_backward, prefill_train)
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "decode_auto_split", "ParallaxError", "LIB_PATH",
-           "EXPORTS", "load_library"]
+__all__ = ["prefill", "prefill_train", "prefill_backward", "ParallaxAttention", "decode",
+           "decode_workspace_size", "decode_auto_split", "ParallaxError", "LIB_PATH", "EXPORTS", "load_library"]

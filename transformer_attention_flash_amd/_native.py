@@ -22,6 +22,9 @@ PLX_DTYPE_BF16 = 1
 # Every symbol include/parallax.h declares.
 EXPORTS = (
     "parallax_fwd_prefill",
+    "parallax_fwd_prefill_train",
+    "parallax_bwd_prefill_workspace_size",
+    "parallax_bwd_prefill",
     "parallax_fwd_decode_workspace_size",
     "parallax_fwd_decode",
     "parallax_fwd_decode_auto_split",
@@ -52,6 +55,14 @@ def load():
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     lib.parallax_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp]
     lib.parallax_fwd_prefill.restype = ctypes.c_int
+    lib.parallax_fwd_prefill_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                               ctypes.c_int, vp]
+    lib.parallax_fwd_prefill_train.restype = ctypes.c_int
+    lib.parallax_bwd_prefill_workspace_size.argtypes = [i32, i32, i32]
+    lib.parallax_bwd_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_bwd_prefill.argtypes = [vp] * 13 + [i32, i32, i32, i32, i32, f32, ctypes.c_int, vp,
+                                                     ctypes.c_size_t, vp]
+    lib.parallax_bwd_prefill.restype = ctypes.c_int
     lib.parallax_fwd_decode_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int, i32]
     lib.parallax_fwd_decode_workspace_size.restype = ctypes.c_size_t
     lib.parallax_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32, ctypes.c_int,

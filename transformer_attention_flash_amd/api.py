@@ -72,6 +72,85 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[tor
     return out
 
 
+def prefill_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor] = None, *,
+                  scale: Optional[float] = None, stream=None):
+    """Causal Parallax prefill that also keeps what the backward needs (bf16).
+
+    Returns (out, out_sa, lse, rbar): out and out_sa shaped like q; lse and
+    rbar fp32 [B, Hq, T] (lse in log2 units); out_sa and rbar are None
+    without rho.
+    """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D [B, H, T, d]")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, T, d] matching q")
+    if rho is not None and rho.shape != q.shape:
+        raise ValueError("rho must have q's shape")
+    _check_tensors(q.dtype, q=q, k=k, v=v, rho=rho)
+    code = _dtype_code(q.dtype)
+    out = torch.empty_like(q)
+    out_sa = None if rho is None else torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    rbar = None if rho is None else torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = N.load().parallax_fwd_prefill_train(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out), _ptr(out_sa),
+                                             _ptr(lse), _ptr(rbar), B, Hq, Hkv, T, d, scale, code,
+                                             _stream(stream))
+    N.check(st, "parallax_fwd_prefill_train")
+    return out, out_sa, lse, rbar
+
+
+def prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout, *, scale: Optional[float] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv, drho) of sum(dout * out) for the causal Parallax
+    prefill, from the tensors prefill_train returned (bf16).  drho is None
+    when rho is."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    _check_tensors(q.dtype, q=q, k=k, v=v, rho=rho, out=out, out_sa=out_sa, dout=dout)
+    _check_tensors(torch.float32, lse=lse, rbar=rbar)
+    code = _dtype_code(q.dtype)
+    lib = N.load()
+    need = lib.parallax_bwd_prefill_workspace_size(B, Hq, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    drho = None if rho is None else torch.empty_like(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.parallax_bwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out), _ptr(out_sa), _ptr(lse),
+                                  _ptr(rbar), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drho),
+                                  B, Hq, Hkv, T, d, scale, code, _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    N.check(st, "parallax_bwd_prefill")
+    return dq, dk, dv, drho
+
+
+class ParallaxAttention(torch.autograd.Function):
+    """torch.autograd wrapper: forward = prefill_train, backward =
+    prefill_backward (bf16, causal).  Marshalling only."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, rho, scale):
+        out, out_sa, lse, rbar = prefill_train(q, k, v, rho, scale=scale)
+        ctx.save_for_backward(q, k, v, rho, out, out_sa, lse, rbar)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, rho, out, out_sa, lse, rbar = ctx.saved_tensors
+        dq, dk, dv, drho = prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout.contiguous(),
+                                            scale=ctx.scale)
+        return dq, dk, dv, drho, None
+
+
 def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype=torch.bfloat16,
                           keys_per_split: int = 0) -> int:
     n = N.load().parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype),

@@ -88,15 +88,13 @@ plx_status_t plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t 
     return PLX_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, const void *rho, void *out,
-                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
-                                  float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
+// Causal prefill forward; the training variant also keeps (out_sa, lse, rbar).
+plx_status_t prefill_impl(const void *q, const void *k, const void *v, const void *rho, void *out, void *out_sa,
+                          float *lse, float *rbar, int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                          float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
     if (!q || !k || !v || !out) return PLX_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(out))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(out) ||
+        !aligned16(out_sa) || !aligned16(lse) || !aligned16(rbar))
         return PLX_ERR_INVALID_ARGUMENT;
     if (T < 1) return PLX_ERR_INVALID_ARGUMENT;
     plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
@@ -110,9 +108,16 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, c
     const size_t es = elem_bytes(dtype);
     const size_t q_bytes = static_cast<size_t>(B) * Hq * T * d * es;
     const size_t kv_bytes = static_cast<size_t>(B) * Hkv * T * d * es;
-    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k, kv_bytes) ||
-        overlaps(out, q_bytes, v, kv_bytes) || overlaps(out, q_bytes, rho, q_bytes))
-        return PLX_ERR_INVALID_ARGUMENT;
+    const size_t st_bytes = static_cast<size_t>(B) * Hq * T * sizeof(float);
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}, {rho, q_bytes}};
+    const Span outs[] = {{out, q_bytes}, {out_sa, q_bytes}, {lse, st_bytes}, {rbar, st_bytes}};
+    for (const Span &o : outs) {
+        for (const Span &x : ins)
+            if (overlaps(o.p, o.n, x.p, x.n)) return PLX_ERR_INVALID_ARGUMENT;
+        for (const Span &x : outs)
+            if (&x != &o && overlaps(o.p, o.n, x.p, x.n)) return PLX_ERR_INVALID_ARGUMENT;
+    }
 
     plx::PrefillParams p;
     p.q = q;
@@ -120,6 +125,9 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, c
     p.v = v;
     p.rho = rho;
     p.out = out;
+    p.out_sa = out_sa;
+    p.lse = lse;
+    p.rbar = rbar;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -128,6 +136,103 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, c
     p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     const hipError_t e =
         plx::launch_prefill(p, bf16, d, G, rho != nullptr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, const void *rho, void *out,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                                  float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
+    return prefill_impl(q, k, v, rho, out, nullptr, nullptr, nullptr, B, Hq, Hkv, T, d, softmax_scale, dtype,
+                        stream);
+}
+
+plx_status_t parallax_fwd_prefill_train(const void *q, const void *k, const void *v, const void *rho, void *out,
+                                        void *out_sa, float *lse, float *rbar, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t T, int32_t d, float softmax_scale,
+                                        plx_dtype_t dtype, plx_stream_t stream) {
+    if (!lse) return PLX_ERR_INVALID_ARGUMENT;
+    if ((rho == nullptr) != (out_sa == nullptr) || (rho == nullptr) != (rbar == nullptr))
+        return PLX_ERR_INVALID_ARGUMENT;
+    if (dtype != PLX_DTYPE_BF16) return PLX_ERR_UNSUPPORTED;
+    return prefill_impl(q, k, v, rho, out, out_sa, lse, rbar, B, Hq, Hkv, T, d, softmax_scale, dtype, stream);
+}
+
+size_t parallax_bwd_prefill_workspace_size(int32_t B, int32_t Hq, int32_t T) {
+    if (B < 1 || Hq < 1 || T < 1) return ~size_t{0};
+    return static_cast<size_t>(B) * Hq * T * 4 * sizeof(float);
+}
+
+plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v, const void *rho, const void *out,
+                                  const void *out_sa, const float *lse, const float *rbar, const void *dout,
+                                  void *dq, void *dk, void *dv, void *drho, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t T, int32_t d, float softmax_scale, plx_dtype_t dtype, void *workspace,
+                                  size_t workspace_bytes, plx_stream_t stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return PLX_ERR_INVALID_ARGUMENT;
+    const bool has_rho = rho != nullptr;
+    if (has_rho != (out_sa != nullptr) || has_rho != (rbar != nullptr) || has_rho != (drho != nullptr))
+        return PLX_ERR_INVALID_ARGUMENT;
+    const void *ptrs[] = {q, k, v, rho, out, out_sa, lse, rbar, dout, dq, dk, dv, drho, workspace};
+    for (const void *x : ptrs)
+        if (!aligned16(x)) return PLX_ERR_INVALID_ARGUMENT;
+    if (T < 1) return PLX_ERR_INVALID_ARGUMENT;
+    plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
+    if (st != PLX_OK) return st;
+    if (dtype != PLX_DTYPE_BF16) return PLX_ERR_UNSUPPORTED;
+    const size_t need = parallax_bwd_prefill_workspace_size(B, Hq, T);
+    if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+    const int G = Hq / Hkv;
+    const int bq = plx::backward_q_block_positions(G);
+    const int kb = plx::backward_k_block_keys();
+    const int64_t n_qblk = (static_cast<int64_t>(T) + bq - 1) / bq;
+    const int64_t n_kblk = (static_cast<int64_t>(T) + kb - 1) / kb;
+    const int64_t units = static_cast<int64_t>(B) * Hkv;
+    const int64_t rows = static_cast<int64_t>(B) * Hq * T;
+    if (units * n_qblk > kMaxGrid || units * n_kblk > kMaxGrid || (rows + 15) / 16 > kMaxGrid)
+        return PLX_ERR_UNSUPPORTED;
+
+    // No output may overlap an input, another output or the workspace.
+    const size_t qb = static_cast<size_t>(rows) * d * 2;
+    const size_t kvb = static_cast<size_t>(B) * Hkv * T * d * 2;
+    const size_t sb = static_cast<size_t>(rows) * sizeof(float);
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{q, qb}, {k, kvb}, {v, kvb}, {rho, qb}, {out, qb}, {out_sa, qb}, {lse, sb}, {rbar, sb},
+                        {dout, qb}, {workspace, need}};
+    const Span outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {drho, qb}};
+    for (const Span &o : outs) {
+        for (const Span &x : ins)
+            if (overlaps(o.p, o.n, x.p, x.n)) return PLX_ERR_INVALID_ARGUMENT;
+        for (const Span &x : outs)
+            if (&x != &o && overlaps(o.p, o.n, x.p, x.n)) return PLX_ERR_INVALID_ARGUMENT;
+    }
+
+    plx::BackwardParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.rho = rho;
+    p.out = out;
+    p.out_sa = out_sa;
+    p.lse = lse;
+    p.rbar = rbar;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.drho = drho;
+    p.rowst = static_cast<float4 *>(workspace);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.T = T;
+    p.n_qblk = static_cast<int32_t>(n_qblk);
+    p.n_kblk = static_cast<int32_t>(n_kblk);
+    p.scale = softmax_scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    const hipError_t e = plx::launch_backward(p, d, G, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

@@ -1,0 +1,531 @@
+// plx_backward.hip -- Parallax attention causal-prefill backward on gfx950
+// (bf16 storage, fp32 accumulation).
+//
+// The forward is o_i = o^SA_i - Sigma^(i)_KV rho_i (the gist.science summary
+// of Parallax, "Method: Parallax / core mechanism"; no boundary term, "key
+// design choices").  Written as o_i = sum_j w_ij v_j with
+// w_ij = p_ij (1 - r_ij + rbar_i), r_ij = rho_i . k_j, rbar_i = sum_j p_ij r_ij,
+// its gradients for an upstream dO are
+//
+//   g_ij  = dO_i . v_j        G_i = dO_i . o^SA_i        D_i = dO_i . o_i + rbar_i G_i
+//   dS_ij = p_ij (g_ij (1 - r_ij + rbar_i) + G_i r_ij - D_i)     (w.r.t. s = scale q.k)
+//   dR_ij = p_ij (G_i - g_ij)                                    (w.r.t. r = rho.k)
+//   dq_i = scale sum_j dS_ij k_j     drho_i = sum_j dR_ij k_j
+//   dk_j = scale sum_i dS_ij q_i + sum_i dR_ij rho_i             dv_j = sum_i w_ij dO_i
+//
+// (derived: dL/dw_ij = g_ij; w depends on p, r and rbar; then the softmax).
+// The pages train with this layer but print no backward pass.  With a zero
+// probe these are FlashAttention's gradients (r = rbar = 0, G = D).
+//
+// Three kernels, FlashAttention-2 style, recomputing p from the forward's
+// per-row log2-sum-exp instead of storing it:
+//   bwd_rowstat_kernel  per row: (lse, rbar, G, D)
+//   bwd_dq_kernel       a workgroup of 8 wavefronts owns 128 query rows (as
+//                       the forward) and streams K/V tiles; dq and drho come
+//                       out of one transposed read of the K tile.
+//   bwd_dkdv_kernel     a workgroup of 8 wavefronts owns 128 keys (16 per
+//                       wavefront, held in registers) and streams 32-row
+//                       tiles of q, rho and dO over the G query heads of the
+//                       KV head, so dk and dv sum over the group in-kernel
+//                       with no atomics.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16; lane l, col = l % 16, grp = l / 16):
+// A row col holds contraction slots 8grp..8grp+7, B column col the same
+// slots, C rows 4grp..4grp+3 of column col.  Slots are a free permutation as
+// long as A and B agree: wherever a GEMM contracts over keys (dq) or query
+// rows (dk, dv), slot e of lane group grp is element 4grp + (e & 3) +
+// 16 (e >> 2) of the 32-slice, which is both how two 16-row C blocks land in
+// a lane and what ds_read_b64_tr_b16 returns (see plx_prefill.hip).
+#include "plx_device.h"
+#include "plx_kernels.h"
+
+namespace plx {
+
+namespace {
+
+constexpr int kBwdWaves = 8;
+constexpr int kBwdKT = 64;   // dq kernel: keys per LDS tile
+constexpr int kBwdQR = 32;   // dk/dv kernel: query rows per LDS step
+constexpr int kRowPad = 16;  // LDS row padding in elements (32 bytes; see the forward)
+
+// ---------------------------------------------------------------------------
+// Row statistics: rowst[row] = (lse, rbar, G, D).  16 lanes per row.
+// ---------------------------------------------------------------------------
+template <int D, bool HAS_RHO>
+__global__ __launch_bounds__(256) void bwd_rowstat_kernel(BackwardParams p) {
+    constexpr int EPL = D / 16;  // elements per lane
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.T;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + threadIdx.x / 16;
+    const int sub = threadIdx.x % 16;
+    float dot_o = 0.f, dot_sa = 0.f;
+    if (row < rows) {
+        const uint16_t *dO = static_cast<const uint16_t *>(p.dout) + row * D + sub * EPL;
+        const uint16_t *o = static_cast<const uint16_t *>(p.out) + row * D + sub * EPL;
+        const uint16_t *osa = HAS_RHO ? static_cast<const uint16_t *>(p.out_sa) + row * D + sub * EPL : nullptr;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            const u32x2 a = *reinterpret_cast<const u32x2 *>(dO + e);
+            const u32x2 b = *reinterpret_cast<const u32x2 *>(o + e);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                dot_o += bf16_to_f32(a[h] & 0xffffu) * bf16_to_f32(b[h] & 0xffffu);
+                dot_o += bf16_to_f32(a[h] >> 16) * bf16_to_f32(b[h] >> 16);
+            }
+            if constexpr (HAS_RHO) {
+                const u32x2 c = *reinterpret_cast<const u32x2 *>(osa + e);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    dot_sa += bf16_to_f32(a[h] & 0xffffu) * bf16_to_f32(c[h] & 0xffffu);
+                    dot_sa += bf16_to_f32(a[h] >> 16) * bf16_to_f32(c[h] >> 16);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        dot_o += __shfl_xor(dot_o, m);
+        if constexpr (HAS_RHO) dot_sa += __shfl_xor(dot_sa, m);
+    }
+    if (row < rows && sub == 0) {
+        const float rbar = HAS_RHO ? p.rbar[row] : 0.f;
+        const float G = HAS_RHO ? dot_sa : dot_o;
+        const float Dsum = HAS_RHO ? dot_o + rbar * G : dot_o;
+        p.rowst[row] = make_float4(p.lse[row], rbar, G, Dsum);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq, drho: per workgroup 8 wavefronts x 16 query rows, K/V tiles of 64 keys.
+// ---------------------------------------------------------------------------
+template <int D, int G, bool HAS_RHO>
+__global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardParams p) {
+    using S = uint16_t;
+    constexpr int KT = kBwdKT;
+    constexpr int PW = 16 / G;            // positions per wavefront
+    constexpr int BQ = PW * kBwdWaves;    // positions per workgroup
+    constexpr int KS = D / 32;
+    constexpr int NKB = KT / 16;
+    constexpr int NU = KT / 32;
+    constexpr int DT = D / 16;
+    constexpr int RS = D + kRowPad;       // LDS row stride of K and V tiles
+    constexpr int NTHR = kBwdWaves * kWave;
+    constexpr int KCH = KT * D / 8;       // 8-element chunks per tile
+    constexpr int NKC = (KCH + NTHR - 1) / NTHR;
+    constexpr bool FULL = KCH % NTHR == 0;
+    static_assert(16 % G == 0, "group size must divide the wavefront's 16 rows");
+
+    __shared__ __attribute__((aligned(16))) S lds_k[2][KT * RS];
+    __shared__ __attribute__((aligned(16))) S lds_v[2][KT * RS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    const int n_units = p.B * p.Hkv;
+    const int qb = p.n_qblk - 1 - static_cast<int>(blockIdx.x) / n_units;  // longest first
+    const int unit = static_cast<int>(blockIdx.x) % n_units;
+    const int b = unit / p.Hkv;
+    const int g = unit % p.Hkv;
+    const int T_len = p.T;
+    const int pos0 = qb * BQ;
+    const int wpos0 = pos0 + wave * PW;
+    const int wpos_last = wpos0 + PW - 1;
+    const int key_end = min(pos0 + BQ, T_len);
+    const int n_tiles = (key_end + KT - 1) / KT;
+
+    const int64_t kv_base = (static_cast<int64_t>(b) * p.Hkv + g) * T_len * static_cast<int64_t>(D);
+    const S *kg = static_cast<const S *>(p.k) + kv_base;
+    const S *vg = static_cast<const S *>(p.v) + kv_base;
+
+    // This lane's row: position wpos0 + col / G of query head g*G + col % G.
+    const int pos = wpos0 + col / G;
+    const int head = g * G + col % G;
+    const int64_t row = (static_cast<int64_t>(b) * p.Hq + head) * T_len + min(pos, T_len - 1);
+    const int64_t roff = row * D;
+    Op8<BF16> qop[KS], dop[KS], rop[HAS_RHO ? KS : 1];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        qop[s] = op8_load(static_cast<const S *>(p.q) + roff + 32 * s + 8 * grp);
+        dop[s] = op8_load(static_cast<const S *>(p.dout) + roff + 32 * s + 8 * grp);
+        if constexpr (HAS_RHO) rop[s] = op8_load(static_cast<const S *>(p.rho) + roff + 32 * s + 8 * grp);
+    }
+    const float4 st = p.rowst[row];
+    const float lse = st.x, rbar = st.y, Gi = st.z, Di = st.w;
+
+    int g_off[NKC], l_off[NKC];
+#pragma unroll
+    for (int n = 0; n < NKC; ++n) {
+        const int c = min(tid + n * NTHR, KCH - 1);
+        g_off[n] = (c / (D / 8)) * D + (c % (D / 8)) * 8;
+        l_off[n] = (c / (D / 8)) * RS + (c % (D / 8)) * 8;
+    }
+    Op8<BF16> kreg[NKC], vreg[NKC];
+    auto load_tile = [&](int j) {
+        const int key0 = j * KT;
+#pragma unroll
+        for (int n = 0; n < NKC; ++n) {
+            const int c = tid + n * NTHR;
+            if (FULL || c < KCH) {
+                if (key0 + KT <= T_len) {
+                    kreg[n] = op8_load(kg + static_cast<int64_t>(key0) * D + g_off[n]);
+                    vreg[n] = op8_load(vg + static_cast<int64_t>(key0) * D + g_off[n]);
+                } else {
+                    const int kk = min(key0 + c / (D / 8), T_len - 1);
+                    const int off = (c % (D / 8)) * 8;
+                    kreg[n] = op8_load(kg + static_cast<int64_t>(kk) * D + off);
+                    vreg[n] = op8_load(vg + static_cast<int64_t>(kk) * D + off);
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < NKC; ++n)
+            if (FULL || tid + n * NTHR < KCH) {
+                store_op8(&lds_k[buf][l_off[n]], kreg[n]);
+                store_op8(&lds_v[buf][l_off[n]], vreg[n]);
+            }
+    };
+
+    f32x4 dqacc[DT], dracc[HAS_RHO ? DT : 1];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+        dqacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_RHO) dracc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    load_tile(0);
+    store_tile(0);
+    for (int j = 0; j < n_tiles; ++j) {
+        const int buf = j & 1;
+        __syncthreads();
+        const bool more = j + 1 < n_tiles;
+        if (more) load_tile(j + 1);
+        const int key0 = j * KT;
+        if (key0 <= wpos_last) {
+            const S *kt = lds_k[buf];
+            const S *vt = lds_v[buf];
+            // S^T = K q^T, R^T = K rho^T, g^T = V dO^T: rows are keys, the
+            // lane's column is its query row.
+            f32x4 sacc[NKB], racc[HAS_RHO ? NKB : 1], gacc[NKB];
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, r = a, gg = a;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const Op8<BF16> kop = op8_load(kt + (16 * kb + col) * RS + 32 * s + 8 * grp);
+                    const Op8<BF16> vop = op8_load(vt + (16 * kb + col) * RS + 32 * s + 8 * grp);
+                    a = mma32(kop, qop[s], a);
+                    if constexpr (HAS_RHO) r = mma32(kop, rop[s], r);
+                    gg = mma32(vop, dop[s], gg);
+                }
+                sacc[kb] = a;
+                if constexpr (HAS_RHO) racc[kb] = r;
+                gacc[kb] = gg;
+            }
+            __builtin_amdgcn_s_setprio(0);
+
+            const bool diag = key0 + KT - 1 > wpos0;
+            const int rel = pos - key0 - 4 * grp;  // key > pos <=> offset > rel
+            float ds[NKB * 4], dr[HAS_RHO ? NKB * 4 : 1];
+#pragma unroll
+            for (int e = 0; e < NKB * 4; ++e) {
+                const int kb = e >> 2, i = e & 3;
+                float pr = fast_exp2(fmaf(sacc[kb][i], p.scale_log2, -lse));
+                if (diag && 16 * kb + i > rel) pr = 0.f;
+                const float gv = gacc[kb][i];
+                if constexpr (HAS_RHO) {
+                    const float rv = racc[kb][i];
+                    ds[e] = p.scale * pr * (gv * (1.f - rv + rbar) + Gi * rv - Di);
+                    dr[e] = pr * (Gi - gv);
+                } else {
+                    ds[e] = p.scale * pr * (gv - Di);
+                }
+            }
+            Op8<BF16> dsop[NU], drop[HAS_RHO ? NU : 1];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = ds[8 * u + e];
+                dsop[u] = op8_pack(w, BF16{});
+                if constexpr (HAS_RHO) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = dr[8 * u + e];
+                    drop[u] = op8_pack(w, BF16{});
+                }
+            }
+            // dq^T += K^T dS^T and drho^T += K^T dR^T: the K tile read
+            // transposed gives, to lane col, dim 16t + col of the keys in the
+            // slot order of dsop.
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const S *a = kt + (32 * u + 4 * grp + (col >> 2)) * RS + 16 * t + 4 * (col & 3);
+                    const Op8<BF16> ktr = op8_load_tr(a, a + 16 * RS);
+                    dqacc[t] = mma32(ktr, dsop[u], dqacc[t]);
+                    if constexpr (HAS_RHO) dracc[t] = mma32(ktr, drop[u], dracc[t]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        if (more) store_tile(buf ^ 1);
+    }
+
+    if (pos < T_len) {
+        S *dq = static_cast<S *>(p.dq) + roff;
+        S *drho = HAS_RHO ? static_cast<S *>(p.drho) + roff : nullptr;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = dqacc[t][i];
+            store4(dq + 16 * t + 4 * grp, y);
+            if constexpr (HAS_RHO) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = dracc[t][i];
+                store4(drho + 16 * t + 4 * grp, y);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: per workgroup 8 wavefronts x 16 keys; steps of 32 query rows of the
+// G heads (row r of KV head g is position r / G of query head g*G + r % G).
+// ---------------------------------------------------------------------------
+template <int D, int G, bool HAS_RHO>
+__global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardParams p) {
+    using S = uint16_t;
+    constexpr int QR = kBwdQR;
+    constexpr int KB = 16 * kBwdWaves;    // keys per workgroup
+    constexpr int KS = D / 32;
+    constexpr int DT = D / 16;
+    constexpr int RS = D + kRowPad;
+    constexpr int NTHR = kBwdWaves * kWave;
+    constexpr int QCH = QR * D / 8;       // 8-element chunks per row tile
+    static_assert(QCH <= NTHR, "one chunk of each tensor per thread");
+    constexpr int NTEN = HAS_RHO ? 3 : 2; // q, dO (, rho)
+
+    __shared__ __attribute__((aligned(16))) S lds_q[2][QR * RS];
+    __shared__ __attribute__((aligned(16))) S lds_d[2][QR * RS];
+    __shared__ __attribute__((aligned(16))) S lds_r[HAS_RHO ? 2 : 1][HAS_RHO ? QR * RS : 8];
+    __shared__ float4 lds_st[2][QR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    const int n_units = p.B * p.Hkv;
+    const int kblk = static_cast<int>(blockIdx.x) / n_units;  // longest first: key block 0 sees every query
+    const int unit = static_cast<int>(blockIdx.x) % n_units;
+    const int b = unit / p.Hkv;
+    const int g = unit % p.Hkv;
+    const int T_len = p.T;
+    const int k0 = kblk * KB;
+    const int kw0 = k0 + 16 * wave;         // this wavefront's first key
+    const int key = kw0 + col;              // this lane's key
+    const int64_t rows_total = static_cast<int64_t>(T_len) * G;
+    const int64_t r0 = static_cast<int64_t>(k0) * G;  // first row that can see key k0
+    const int n_steps = static_cast<int>((rows_total - r0 + QR - 1) / QR);
+
+    const int64_t kv_base = (static_cast<int64_t>(b) * p.Hkv + g) * T_len * static_cast<int64_t>(D);
+    // The wavefront's keys as the B operand (column = key): K[key][dims].
+    Op8<BF16> kop[KS], vop[KS];
+    {
+        const int kk = min(key, T_len - 1);
+        const S *kr = static_cast<const S *>(p.k) + kv_base + static_cast<int64_t>(kk) * D;
+        const S *vr = static_cast<const S *>(p.v) + kv_base + static_cast<int64_t>(kk) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kop[s] = op8_load(kr + 32 * s + 8 * grp);
+            vop[s] = op8_load(vr + 32 * s + 8 * grp);
+        }
+    }
+
+    // Row tile loader: thread tid moves chunk tid of each tensor (if any).
+    const bool loader = tid < QCH;
+    const int lrow = tid / (D / 8), lcol = (tid % (D / 8)) * 8;
+    Op8<BF16> stg[NTEN];
+    float4 stst = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto row_ptr_off = [&](int64_t r) {  // element offset of row r of the KV group in a [B, Hq, T, D] tensor
+        const int64_t rr = min(r, rows_total - 1);
+        const int64_t pp = rr / G;
+        const int hh = g * G + static_cast<int>(rr % G);
+        return ((static_cast<int64_t>(b) * p.Hq + hh) * T_len + pp);
+    };
+    auto load_step = [&](int step) {
+        const int64_t rs0 = r0 + static_cast<int64_t>(step) * QR;
+        if (loader) {
+            const int64_t off = row_ptr_off(rs0 + lrow) * D + lcol;
+            stg[0] = op8_load(static_cast<const S *>(p.q) + off);
+            stg[1] = op8_load(static_cast<const S *>(p.dout) + off);
+            if constexpr (HAS_RHO) stg[2] = op8_load(static_cast<const S *>(p.rho) + off);
+        }
+        if (tid < QR) stst = p.rowst[row_ptr_off(rs0 + tid)];
+    };
+    auto store_step = [&](int buf) {
+        if (loader) {
+            store_op8(&lds_q[buf][lrow * RS + lcol], stg[0]);
+            store_op8(&lds_d[buf][lrow * RS + lcol], stg[1]);
+            if constexpr (HAS_RHO) store_op8(&lds_r[buf][lrow * RS + lcol], stg[2]);
+        }
+        if (tid < QR) lds_st[buf][tid] = stst;
+    };
+
+    f32x4 dkacc[DT], dvacc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+        dkacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dvacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (n_steps > 0) {
+        load_step(0);
+        store_step(0);
+    }
+    for (int step = 0; step < n_steps; ++step) {
+        const int buf = step & 1;
+        __syncthreads();
+        const bool more = step + 1 < n_steps;
+        if (more) load_step(step + 1);
+        const int64_t rs0 = r0 + static_cast<int64_t>(step) * QR;
+        // Rows of this step reach position (rs0 + QR - 1) / G; the wavefront's
+        // keys start at kw0.  Skip (wavefront-uniformly) when no row can see them.
+        if ((rs0 + QR - 1) / G >= kw0 && kw0 < T_len) {
+            const S *qt = lds_q[buf];
+            const S *dt = lds_d[buf];
+            const S *rt = HAS_RHO ? lds_r[buf] : nullptr;
+            // S = q K^T, R = rho K^T, g = dO V^T: rows are query rows (two
+            // 16-row blocks), the lane's column is its key.
+            f32x4 sacc[2], racc[HAS_RHO ? 2 : 1], gacc[2];
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, r = a, gg = a;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int off = (16 * qb + col) * RS + 32 * s + 8 * grp;
+                    a = mma32(op8_load(qt + off), kop[s], a);
+                    if constexpr (HAS_RHO) r = mma32(op8_load(rt + off), kop[s], r);
+                    gg = mma32(op8_load(dt + off), vop[s], gg);
+                }
+                sacc[qb] = a;
+                if constexpr (HAS_RHO) racc[qb] = r;
+                gacc[qb] = gg;
+            }
+            __builtin_amdgcn_s_setprio(0);
+
+            float w[8], ds[8], dr[HAS_RHO ? 8 : 1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int qb = e >> 2, i = e & 3;
+                const int lr = 16 * qb + 4 * grp + i;  // row within the step
+                const int64_t r = rs0 + lr;
+                const float4 st = lds_st[buf][lr];     // (lse, rbar, G, D)
+                const bool valid = r < rows_total && key <= static_cast<int>(r / G) && key < T_len;
+                float pr = fast_exp2(fmaf(sacc[qb][i], p.scale_log2, -st.x));
+                if (!valid) pr = 0.f;
+                const float gv = gacc[qb][i];
+                if constexpr (HAS_RHO) {
+                    const float rv = racc[qb][i];
+                    const float f = 1.f - rv + st.y;
+                    w[e] = pr * f;
+                    ds[e] = p.scale * pr * (gv * f + st.z * rv - st.w);
+                    dr[e] = pr * (st.z - gv);
+                } else {
+                    w[e] = pr;
+                    ds[e] = p.scale * pr * (gv - st.w);
+                }
+            }
+            const Op8<BF16> wop = op8_pack(w, BF16{});
+            const Op8<BF16> dsop = op8_pack(ds, BF16{});
+            Op8<BF16> drop;
+            if constexpr (HAS_RHO) drop = op8_pack(dr, BF16{});
+            // dv^T += dO^T W, dk^T += q^T dS + rho^T dR: the row tiles read
+            // transposed give, to lane col, dim 16t + col of the rows in the
+            // slot order of wop/dsop/drop.
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const int off = (4 * grp + (col >> 2)) * RS + 16 * t + 4 * (col & 3);
+                dvacc[t] = mma32(op8_load_tr(dt + off, dt + off + 16 * RS), wop, dvacc[t]);
+                dkacc[t] = mma32(op8_load_tr(qt + off, qt + off + 16 * RS), dsop, dkacc[t]);
+                if constexpr (HAS_RHO) dkacc[t] = mma32(op8_load_tr(rt + off, rt + off + 16 * RS), drop, dkacc[t]);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        if (more) store_step(buf ^ 1);
+    }
+
+    if (key < T_len) {
+        const int64_t off = kv_base + static_cast<int64_t>(key) * D;
+        S *dk = static_cast<S *>(p.dk) + off;
+        S *dv = static_cast<S *>(p.dv) + off;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = dkacc[t][i];
+            store4(dk + 16 * t + 4 * grp, y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = dvacc[t][i];
+            store4(dv + 16 * t + 4 * grp, y);
+        }
+    }
+}
+
+template <int D, int G, bool R>
+hipError_t launch_bwd_r(const BackwardParams &p, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.T;
+    hipLaunchKernelGGL((bwd_rowstat_kernel<D, R>), dim3(static_cast<uint32_t>((rows + 15) / 16)), dim3(256), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t units = static_cast<int64_t>(p.B) * p.Hkv;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G, R>), dim3(static_cast<uint32_t>(units * p.n_qblk)),
+                       dim3(kBwdWaves * kWave), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, R>), dim3(static_cast<uint32_t>(units * p.n_kblk)),
+                       dim3(kBwdWaves * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_bwd_g(const BackwardParams &p, hipStream_t stream) {
+    return p.rho ? launch_bwd_r<D, G, true>(p, stream) : launch_bwd_r<D, G, false>(p, stream);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BackwardParams &p, int G, hipStream_t stream) {
+    switch (G) {
+    case 1: return launch_bwd_g<D, 1>(p, stream);
+    case 2: return launch_bwd_g<D, 2>(p, stream);
+    case 4: return launch_bwd_g<D, 4>(p, stream);
+    case 8: return launch_bwd_g<D, 8>(p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int backward_q_block_positions(int G) { return 16 / G * kBwdWaves; }
+int backward_k_block_keys() { return 16 * kBwdWaves; }
+
+hipError_t launch_backward(const BackwardParams &p, int D, int G, hipStream_t stream) {
+    switch (D) {
+    case 64: return launch_bwd_d<64>(p, G, stream);
+    case 128: return launch_bwd_d<128>(p, G, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace plx

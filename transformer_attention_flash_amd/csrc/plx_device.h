@@ -157,6 +157,23 @@ __device__ __forceinline__ float op8_sum_acc(const Op8<F32> &o, float acc) {
 template <class T>
 __device__ __forceinline__ float op8_sum(const Op8<T> &o) { return op8_sum_acc(o, 0.f); }
 
+// Eight storage elements to memory (LDS or global; 16-byte aligned).
+__device__ __forceinline__ void store_op8(uint16_t *dst, const Op8<BF16> &o) {
+    *reinterpret_cast<u32x4 *>(dst) = o.w;
+}
+__device__ __forceinline__ void store_op8(float *dst, const Op8<F32> &o) {
+    reinterpret_cast<f32x4 *>(dst)[0] = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+    reinterpret_cast<f32x4 *>(dst)[1] = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
+}
+
+// Four fp32 results to four contiguous storage elements (RNE for bf16).
+__device__ __forceinline__ void store4(uint16_t *dst, const float (&y)[4]) {
+    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
+}
+__device__ __forceinline__ void store4(float *dst, const float (&y)[4]) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+}
+
 // Wave-uniform "any lane": true on every lane if pred holds on one.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

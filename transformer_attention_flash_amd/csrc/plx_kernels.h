@@ -29,9 +29,27 @@ struct PrefillParams {
     const void *v;
     const void *rho;    // [B, Hq, T, D] (unused by the softmax-only kernel)
     void *out;          // [B, Hq, T, D]
+    // Training forward only (all null otherwise): what the backward needs.
+    void *out_sa;       // [B, Hq, T, D] softmax-attention part A/l (null: not kept)
+    float *lse;         // [B, Hq, T] log2 of sum_j 2^(s_ij * log2 e), s = scale * q.k
+    float *rbar;        // [B, Hq, T] c/l = sum_j p_ij (rho_i . k_j)
     int32_t B, Hq, Hkv, T;
     int32_t n_qblk;     // query blocks per (b, kv head)
     float scale_log2;
+};
+
+struct BackwardParams {
+    const void *q, *k, *v, *rho;   // forward inputs (rho null: softmax only)
+    const void *out, *out_sa;      // forward outputs (out_sa null when rho is)
+    const float *lse, *rbar;       // forward row statistics
+    const void *dout;              // [B, Hq, T, D] upstream gradient
+    void *dq, *dk, *dv, *drho;     // gradients, shaped like q, k, v, rho
+    float4 *rowst;                 // workspace [B, Hq, T]: (lse, rbar, G, Dsum)
+    int32_t B, Hq, Hkv, T;
+    int32_t n_qblk;                // dq kernel: query blocks per (b, kv head)
+    int32_t n_kblk;                // dk/dv kernel: key blocks per (b, kv head)
+    float scale;                   // softmax scale
+    float scale_log2;              // softmax scale * log2(e)
 };
 
 // Both return the first launch error (hipSuccess when everything queued).
@@ -41,5 +59,10 @@ hipError_t launch_prefill(const PrefillParams &p, bool bf16, int D, int G, bool 
 
 // Query positions one prefill workgroup covers for group size G.
 int prefill_block_positions(bool bf16, int G);
+
+// Prefill backward (bf16): row statistics, then dq/drho and dk/dv.
+hipError_t launch_backward(const BackwardParams &p, int D, int G, hipStream_t stream);
+int backward_q_block_positions(int G);
+int backward_k_block_keys();
 
 }  // namespace plx

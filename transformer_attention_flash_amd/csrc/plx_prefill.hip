@@ -65,21 +65,6 @@ __device__ __forceinline__ void store_vt4(float *dst, const Op8<F32> (&v)[4], in
     *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
 }
 
-__device__ __forceinline__ void store_op8(uint16_t *dst, const Op8<BF16> &o) {
-    *reinterpret_cast<u32x4 *>(dst) = o.w;
-}
-__device__ __forceinline__ void store_op8(float *dst, const Op8<F32> &o) {
-    reinterpret_cast<f32x4 *>(dst)[0] = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
-    reinterpret_cast<f32x4 *>(dst)[1] = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
-}
-
-__device__ __forceinline__ void store4(uint16_t *dst, const float (&y)[4]) {
-    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
-}
-__device__ __forceinline__ void store4(float *dst, const float (&y)[4]) {
-    *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
-}
-
 }  // namespace
 
 template <class T, int D, int G, bool HAS_RHO>
@@ -434,12 +419,14 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
             const float inv = 1.f / l;
             const float cbar = c * inv;
             S *o = static_cast<S *>(p.out) + qoff[nb];
+            S *osa_out = p.out_sa ? static_cast<S *>(p.out_sa) + qoff[nb] : nullptr;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
-                float y[4];
+                float y[4], ysa[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float osa = acc_a[nb][t][i] * inv;
+                    ysa[i] = osa;
                     if constexpr (HAS_RHO) {
                         const float corr = acc_b[nb][t][i] * inv - cbar * osa;
                         y[i] = osa - corr;
@@ -448,6 +435,14 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                     }
                 }
                 store4(o + 16 * t + 4 * grp, y);
+                if (osa_out) store4(osa_out + 16 * t + 4 * grp, ysa);
+            }
+            // Training forward: the row's log2-sum-exp (P = 2^(s log2e - m)
+            // summed to l, so log2 sum_j 2^(s_j log2e) = m + log2 l) and rbar.
+            if (p.lse != nullptr && grp == 0) {
+                const int64_t row = qoff[nb] / D;
+                p.lse[row] = m_run[nb] + log2f(l);
+                if (p.rbar) p.rbar[row] = cbar;
             }
         }
     }

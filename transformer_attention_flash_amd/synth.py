@@ -84,6 +84,13 @@ def make_prefill(B, Hq, Hkv, T, d, dtype, device, seed: int = 0, rho_std: float 
     return out
 
 
+def make_upstream_grad(shape, dtype, device, seed: int = 0):
+    """An upstream gradient dO ~ N(0, 1) (the backward's second input), drawn
+    from its own generator seeded with 1000 + seed so it does not disturb the
+    forward inputs' draw order."""
+    return _fill_normal(torch.empty(shape, dtype=dtype, device=device), _generator(device, 1000 + seed))
+
+
 def make_decode(B, Hq, Hkv, L, d, dtype, device, seed: int = 0, rho_std: float = RHO_STD):
     """q, rho [B, Hq, d]; contiguous k, v [B, Hkv, L, d]."""
     g = _generator(device, seed)
