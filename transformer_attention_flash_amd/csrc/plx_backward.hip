@@ -24,7 +24,7 @@
 //                       the forward) and streams K/V tiles; dq and drho come
 //                       out of one transposed read of the K tile.
 //   bwd_dkdv_kernel     a workgroup of 8 wavefronts owns 128 keys (16 per
-//                       wavefront, held in registers) and streams 32-row
+//                       wavefront, held in registers) and streams 64-row
 //                       tiles of q, rho and dO over the G query heads of the
 //                       KV head, so dk and dv sum over the group in-kernel
 //                       with no atomics.
@@ -45,8 +45,24 @@ namespace {
 
 constexpr int kBwdWaves = 8;
 constexpr int kBwdKT = 64;   // dq kernel: keys per LDS tile
-constexpr int kBwdQR = 32;   // dk/dv kernel: query rows per LDS step
+constexpr int kBwdQR = 64;   // dk/dv kernel: query rows per LDS step
 constexpr int kRowPad = 16;  // LDS row padding in elements (32 bytes; see the forward)
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+
+// Workgroup id -> (unit = (b, kv head), block index), blocks of a unit in
+// ascending order.  Workgroup ids are dealt to the XCDs round-robin; when the
+// units divide by 8, XCD x runs units x, x + 8, ... one after another, so the
+// workgroups sharing a unit's streamed tensors sit behind the same L2.
+__device__ __forceinline__ void block_order(int id, int n_units, int n_blk, int *unit, int *blk) {
+    if (n_units % kXcds == 0) {
+        const int xcd = id % kXcds, slot = id / kXcds;
+        *blk = slot % n_blk;
+        *unit = xcd + kXcds * (slot / n_blk);
+    } else {
+        *blk = id / n_units;
+        *unit = id % n_units;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Row statistics: rowst[row] = (lse, rbar, G, D).  16 lanes per row.
@@ -123,9 +139,9 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    const int n_units = p.B * p.Hkv;
-    const int qb = p.n_qblk - 1 - static_cast<int>(blockIdx.x) / n_units;  // longest first
-    const int unit = static_cast<int>(blockIdx.x) % n_units;
+    int qb, unit;
+    block_order(static_cast<int>(blockIdx.x), p.B * p.Hkv, p.n_qblk, &unit, &qb);
+    qb = p.n_qblk - 1 - qb;  // longest first
     const int b = unit / p.Hkv;
     const int g = unit % p.Hkv;
     const int T_len = p.T;
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: per workgroup 8 wavefronts x 16 keys; steps of 32 query rows of the
+// dk, dv: per workgroup 8 wavefronts x 16 keys; steps of 64 query rows of the
 // G heads (row r of KV head g is position r / G of query head g*G + r % G).
 // ---------------------------------------------------------------------------
 template <int D, int G, bool HAS_RHO>
@@ -309,8 +325,11 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
     constexpr int RS = D + kRowPad;
     constexpr int NTHR = kBwdWaves * kWave;
     constexpr int QCH = QR * D / 8;       // 8-element chunks per row tile
-    static_assert(QCH <= NTHR, "one chunk of each tensor per thread");
+    constexpr int NQC = (QCH + NTHR - 1) / NTHR;
+    constexpr bool QFULL = QCH % NTHR == 0;
     constexpr int NTEN = HAS_RHO ? 3 : 2; // q, dO (, rho)
+    constexpr int NQB = QR / 16;          // 16-row blocks per step
+    constexpr int NUQ = QR / 32;          // 32-row slices per step
 
     __shared__ __attribute__((aligned(16))) S lds_q[2][QR * RS];
     __shared__ __attribute__((aligned(16))) S lds_d[2][QR * RS];
@@ -323,9 +342,8 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    const int n_units = p.B * p.Hkv;
-    const int kblk = static_cast<int>(blockIdx.x) / n_units;  // longest first: key block 0 sees every query
-    const int unit = static_cast<int>(blockIdx.x) % n_units;
+    int kblk, unit;  // key block 0 sees every query row: it goes first
+    block_order(static_cast<int>(blockIdx.x), p.B * p.Hkv, p.n_kblk, &unit, &kblk);
     const int b = unit / p.Hkv;
     const int g = unit % p.Hkv;
     const int T_len = p.T;
@@ -335,6 +353,12 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
     const int64_t rows_total = static_cast<int64_t>(T_len) * G;
     const int64_t r0 = static_cast<int64_t>(k0) * G;  // first row that can see key k0
     const int n_steps = static_cast<int>((rows_total - r0 + QR - 1) / QR);
+    // Steps walk the rows from the last one backwards on a grid common to all
+    // key blocks (step s covers rows rows_total - (s+1) QR .. rows_total - s QR - 1),
+    // so the concurrently running key blocks of one KV head read the same
+    // tile at about the same time and it is fetched into L2 once.  Rows
+    // before r0 in the last step (negative indices included) are masked.
+    auto step_row0 = [&](int step) { return rows_total - static_cast<int64_t>(step + 1) * QR; };
 
     const int64_t kv_base = (static_cast<int64_t>(b) * p.Hkv + g) * T_len * static_cast<int64_t>(D);
     // The wavefront's keys as the B operand (column = key): K[key][dims].
@@ -350,32 +374,39 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
         }
     }
 
-    // Row tile loader: thread tid moves chunk tid of each tensor (if any).
-    const bool loader = tid < QCH;
-    const int lrow = tid / (D / 8), lcol = (tid % (D / 8)) * 8;
-    Op8<BF16> stg[NTEN];
+    // Row tile loader: thread tid moves chunks tid, tid + NTHR, ... of each tensor.
+    Op8<BF16> stg[NQC][NTEN];
     float4 stst = make_float4(0.f, 0.f, 0.f, 0.f);
     auto row_ptr_off = [&](int64_t r) {  // element offset of row r of the KV group in a [B, Hq, T, D] tensor
-        const int64_t rr = min(r, rows_total - 1);
+        const int64_t rr = min(max(r, int64_t{0}), rows_total - 1);
         const int64_t pp = rr / G;
         const int hh = g * G + static_cast<int>(rr % G);
         return ((static_cast<int64_t>(b) * p.Hq + hh) * T_len + pp);
     };
     auto load_step = [&](int step) {
-        const int64_t rs0 = r0 + static_cast<int64_t>(step) * QR;
-        if (loader) {
-            const int64_t off = row_ptr_off(rs0 + lrow) * D + lcol;
-            stg[0] = op8_load(static_cast<const S *>(p.q) + off);
-            stg[1] = op8_load(static_cast<const S *>(p.dout) + off);
-            if constexpr (HAS_RHO) stg[2] = op8_load(static_cast<const S *>(p.rho) + off);
+        const int64_t rs0 = step_row0(step);
+#pragma unroll
+        for (int n = 0; n < NQC; ++n) {
+            const int c = tid + n * NTHR;
+            if (QFULL || c < QCH) {
+                const int64_t off = row_ptr_off(rs0 + c / (D / 8)) * D + (c % (D / 8)) * 8;
+                stg[n][0] = op8_load(static_cast<const S *>(p.q) + off);
+                stg[n][1] = op8_load(static_cast<const S *>(p.dout) + off);
+                if constexpr (HAS_RHO) stg[n][2] = op8_load(static_cast<const S *>(p.rho) + off);
+            }
         }
         if (tid < QR) stst = p.rowst[row_ptr_off(rs0 + tid)];
     };
     auto store_step = [&](int buf) {
-        if (loader) {
-            store_op8(&lds_q[buf][lrow * RS + lcol], stg[0]);
-            store_op8(&lds_d[buf][lrow * RS + lcol], stg[1]);
-            if constexpr (HAS_RHO) store_op8(&lds_r[buf][lrow * RS + lcol], stg[2]);
+#pragma unroll
+        for (int n = 0; n < NQC; ++n) {
+            const int c = tid + n * NTHR;
+            if (QFULL || c < QCH) {
+                const int lo = (c / (D / 8)) * RS + (c % (D / 8)) * 8;
+                store_op8(&lds_q[buf][lo], stg[n][0]);
+                store_op8(&lds_d[buf][lo], stg[n][1]);
+                if constexpr (HAS_RHO) store_op8(&lds_r[buf][lo], stg[n][2]);
+            }
         }
         if (tid < QR) lds_st[buf][tid] = stst;
     };
@@ -396,19 +427,19 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
         __syncthreads();
         const bool more = step + 1 < n_steps;
         if (more) load_step(step + 1);
-        const int64_t rs0 = r0 + static_cast<int64_t>(step) * QR;
+        const int64_t rs0 = step_row0(step);
         // Rows of this step reach position (rs0 + QR - 1) / G; the wavefront's
         // keys start at kw0.  Skip (wavefront-uniformly) when no row can see them.
         if ((rs0 + QR - 1) / G >= kw0 && kw0 < T_len) {
             const S *qt = lds_q[buf];
             const S *dt = lds_d[buf];
             const S *rt = HAS_RHO ? lds_r[buf] : nullptr;
-            // S = q K^T, R = rho K^T, g = dO V^T: rows are query rows (two
+            // S = q K^T, R = rho K^T, g = dO V^T: rows are query rows (NQB
             // 16-row blocks), the lane's column is its key.
-            f32x4 sacc[2], racc[HAS_RHO ? 2 : 1], gacc[2];
+            f32x4 sacc[NQB], racc[HAS_RHO ? NQB : 1], gacc[NQB];
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < NQB; ++qb) {
                 f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, r = a, gg = a;
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
@@ -423,14 +454,14 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
             }
             __builtin_amdgcn_s_setprio(0);
 
-            float w[8], ds[8], dr[HAS_RHO ? 8 : 1];
+            float w[4 * NQB], ds[4 * NQB], dr[HAS_RHO ? 4 * NQB : 1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 4 * NQB; ++e) {
                 const int qb = e >> 2, i = e & 3;
                 const int lr = 16 * qb + 4 * grp + i;  // row within the step
                 const int64_t r = rs0 + lr;
                 const float4 st = lds_st[buf][lr];     // (lse, rbar, G, D)
-                const bool valid = r < rows_total && key <= static_cast<int>(r / G) && key < T_len;
+                const bool valid = r >= r0 && key <= static_cast<int>(r / G) && key < T_len;
                 float pr = fast_exp2(fmaf(sacc[qb][i], p.scale_log2, -st.x));
                 if (!valid) pr = 0.f;
                 const float gv = gacc[qb][i];
@@ -445,20 +476,37 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
                     ds[e] = p.scale * pr * (gv - st.w);
                 }
             }
-            const Op8<BF16> wop = op8_pack(w, BF16{});
-            const Op8<BF16> dsop = op8_pack(ds, BF16{});
-            Op8<BF16> drop;
-            if constexpr (HAS_RHO) drop = op8_pack(dr, BF16{});
+            Op8<BF16> wop[NUQ], dsop[NUQ], drop[HAS_RHO ? NUQ : 1];
+#pragma unroll
+            for (int u = 0; u < NUQ; ++u) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = w[8 * u + e];
+                wop[u] = op8_pack(x, BF16{});
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = ds[8 * u + e];
+                dsop[u] = op8_pack(x, BF16{});
+                if constexpr (HAS_RHO) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = dr[8 * u + e];
+                    drop[u] = op8_pack(x, BF16{});
+                }
+            }
             // dv^T += dO^T W, dk^T += q^T dS + rho^T dR: the row tiles read
             // transposed give, to lane col, dim 16t + col of the rows in the
-            // slot order of wop/dsop/drop.
+            // slot order of wop/dsop/drop (slice u: rows 32u + 4grp + 0..3
+            // and the same + 16).
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const int off = (4 * grp + (col >> 2)) * RS + 16 * t + 4 * (col & 3);
-                dvacc[t] = mma32(op8_load_tr(dt + off, dt + off + 16 * RS), wop, dvacc[t]);
-                dkacc[t] = mma32(op8_load_tr(qt + off, qt + off + 16 * RS), dsop, dkacc[t]);
-                if constexpr (HAS_RHO) dkacc[t] = mma32(op8_load_tr(rt + off, rt + off + 16 * RS), drop, dkacc[t]);
+            for (int u = 0; u < NUQ; ++u) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const int off = (32 * u + 4 * grp + (col >> 2)) * RS + 16 * t + 4 * (col & 3);
+                    dvacc[t] = mma32(op8_load_tr(dt + off, dt + off + 16 * RS), wop[u], dvacc[t]);
+                    dkacc[t] = mma32(op8_load_tr(qt + off, qt + off + 16 * RS), dsop[u], dkacc[t]);
+                    if constexpr (HAS_RHO)
+                        dkacc[t] = mma32(op8_load_tr(rt + off, rt + off + 16 * RS), drop[u], dkacc[t]);
+                }
             }
         }
         __builtin_amdgcn_s_setprio(0);
