@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
-"""Benchmark of the Parallax attention forward on one MI355X.
+"""Benchmark of Parallax attention on one MI355X.
 
 One JSON line on stdout.  The headline (`value`) is decode KV HBM throughput
 on the decode workload (B=64, Hq=16, Hkv=8, d=128, 4096 cached keys per
 sequence, bf16): one step is one call of parallax_fwd_decode over the whole
 batch (split-KV kernel + merge kernel).  The second half of the metric, the
 causal prefill (B=8, T=4096, Hq=16, Hkv=8, d=128, bf16), is timed the same way
-and reported under "prefill" with its MFMA roofline.
+and reported under "prefill" with its MFMA roofline; the prefill backward
+(parallax_bwd_prefill on the same tensors) under "prefill"/"backward".
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Several input sets are rotated so that no step finds its K/V in the 256 MB
@@ -144,6 +145,34 @@ def cpu_baseline_prefill(x, w, budget_s: float):
                       f"0..{w.T - 1}), fp64 expanded form, {spent:.1f} s"}
 
 
+def cpu_baseline_backward(x, dout, w):
+    """The backward oracle (closed form, numpy fp64 on the host's BLAS) on one
+    whole KV-head group of the prefill workload; returns its TFLOP/s on the
+    same 8-GEMM count as the GPU figure."""
+    import numpy as np
+    from oracle import grad as ograd
+
+    G = w.Hq // w.Hkv
+    b, g = 0, 0
+    hs = slice(g * G, (g + 1) * G)
+    h = {n: x[n][b:b + 1, hs].double().cpu().numpy() for n in ("q", "rho")}
+    kk = x["k"][b:b + 1, g:g + 1].double().cpu().numpy()
+    vv = x["v"][b:b + 1, g:g + 1].double().cpu().numpy()
+    do = dout[b:b + 1, hs].double().cpu().numpy()
+    t0 = time.perf_counter()
+    ograd.grad_expanded(h["q"], kk, vv, h["rho"], do, 1.0 / np.sqrt(w.d), groups=[(0, 0)])
+    dt = time.perf_counter() - t0
+    flops = 8 * 2 * w.d * G * w.T * (w.T + 1) // 2
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except ImportError:
+        cores = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one KV-head group ({G} query heads x {w.T} positions, batch 0, kv head 0), "
+                      f"closed-form fp64 gradients with numpy, {dt:.1f} s"}
+
+
 def run_sweep(args, torch, plx, synth):
     """Decode sweep, Parallax against the softmax-only path (rho = NULL) of the
     same library: batch x context over the pages' range (batch 1..2048,
@@ -204,6 +233,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=20)
+    ap.add_argument("--backward-warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
                     help="decode sweep: Parallax vs softmax-only over batch x context (JSON lines)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -342,6 +374,43 @@ def main():
         if not args.no_cpu_baseline:
             log("prefill CPU baseline (oracle)")
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
+
+        # ---------------- prefill backward (training step of the layer) ----------------
+        if not args.no_backward:
+            x = psets[0]
+            dout = synth.make_upstream_grad(tuple(x["q"].shape), pw.dtype, dev)
+            fw = plx.prefill_train(x["q"], x["k"], x["v"], x["rho"])
+            ws = torch.empty(max(16, pw.B * pw.Hq * pw.T * 16), dtype=torch.uint8, device=dev)
+
+            def backward_step(i):
+                plx.prefill_backward(x["q"], x["k"], x["v"], x["rho"], *fw, dout, workspace=ws)
+
+            def train_forward_step(i):
+                plx.prefill_train(x["q"], x["k"], x["v"], x["rho"])
+
+            bsecs, bper = time_steps(backward_step, args.backward_steps, args.backward_warmup, torch)
+            fsecs, _ = time_steps(train_forward_step, args.backward_steps, args.backward_warmup, torch)
+            # Algorithmic work: 8 GEMM-equivalents of 2d flops per causal pair
+            # (recomputed S and R, g = dO.v, dV, dQ, dK from dS and from dR,
+            # dRho); the kernels execute 11, since dq and dk/dv each recompute
+            # S, R and g.
+            bflops = 8 * 2 * pw.d * pairs
+            btf = bflops / (bsecs / args.backward_steps) / 1e12
+            log(f"backward: {bsecs / args.backward_steps * 1e3:.3f} ms/step, {btf:.1f} TFLOP/s; training forward "
+                f"{fsecs / args.backward_steps * 1e3:.3f} ms")
+            result["prefill"]["backward"] = {
+                "value": round(btf, 2), "unit": "TFLOP/s", "ms_per_step": round(bsecs / args.backward_steps * 1e3, 4),
+                "steps": args.backward_steps, "warmup": args.backward_warmup,
+                "us_per_step_median": round(sorted(bper)[len(bper) // 2] * 1e3, 2),
+                "algorithmic_flops_per_step": bflops, "executed_gemm_equivalents": 11,
+                "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(btf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": "bwd_rowstat + bwd_dq + bwd_dkdv (one parallax_bwd_prefill call)"},
+                "training_forward_ms": round(fsecs / args.backward_steps * 1e3, 4),
+            }
+            if not args.no_cpu_baseline:
+                log("backward CPU baseline (oracle)")
+                result["prefill"]["backward"]["cpu_baseline"] = cpu_baseline_backward(x, dout, pw)
 
     print(json.dumps(result), flush=True)
 
