@@ -7,7 +7,9 @@ sequence, bf16): one step is one call of parallax_fwd_decode over the whole
 batch (split-KV kernel + merge kernel).  The second half of the metric, the
 causal prefill (B=8, T=4096, Hq=16, Hkv=8, d=128, bf16), is timed the same way
 and reported under "prefill" with its MFMA roofline; the prefill backward
-(parallax_bwd_prefill on the same tensors) under "prefill"/"backward".
+(parallax_bwd_prefill on the same tensors) under "prefill"/"backward", and the
+fused q/k/v/probe projection of the same layer under "prefill"/"projection"
+(with torch's library GEMM time for the same product as context).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Several input sets are rotated so that no step finds its K/V in the 256 MB
@@ -234,6 +236,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-projection", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--backward-warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
@@ -374,6 +377,36 @@ def main():
         if not args.no_cpu_baseline:
             log("prefill CPU baseline (oracle)")
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
+
+        # ---------------- fused q/k/v/probe projection of the same layer ----------------
+        if not args.no_projection:
+            dm = pw.Hq * pw.d
+            px, pwt = synth.make_projection(pw.B, pw.T, dm, pw.Hq, pw.Hkv, pw.d, pw.dtype, dev)
+
+            def projection_step(i):
+                plx.qkvr_projection(px, pwt, pw.Hq, pw.Hkv, pw.d)
+
+            x2 = px.reshape(pw.B * pw.T, dm)
+            wt_t = pwt.t()
+
+            def library_gemm_step(i):
+                torch.matmul(x2, wt_t)
+
+            jsecs, _ = time_steps(projection_step, args.prefill_steps, args.prefill_warmup, torch)
+            lsecs, _ = time_steps(library_gemm_step, args.prefill_steps, args.prefill_warmup, torch)
+            jflops = 2 * pw.B * pw.T * (2 * pw.Hq + 2 * pw.Hkv) * pw.d * dm
+            jtf = jflops / (jsecs / args.prefill_steps) / 1e12
+            log(f"projection: {jsecs / args.prefill_steps * 1e3:.3f} ms, {jtf:.1f} TFLOP/s; library GEMM alone "
+                f"{lsecs / args.prefill_steps * 1e3:.3f} ms")
+            result["prefill"]["projection"] = {
+                "value": round(jtf, 2), "unit": "TFLOP/s", "ms_per_step": round(jsecs / args.prefill_steps * 1e3, 4),
+                "shape": {"tokens": pw.B * pw.T, "d_model": dm, "features": (2 * pw.Hq + 2 * pw.Hkv) * pw.d},
+                "roofline": {"bound": "mfma", "achieved": round(jtf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(jtf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": "projection_kernel (one parallax_qkvr_projection call)"},
+                "context_library_gemm_ms": round(lsecs / args.prefill_steps * 1e3, 4),
+            }
+            del px, pwt, x2, wt_t
 
         # ---------------- prefill backward (training step of the layer) ----------------
         if not args.no_backward:

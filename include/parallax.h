@@ -181,6 +181,31 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v,
                                   size_t workspace_bytes, plx_stream_t stream);
 
 /*
+ * Fused q/k/v/probe projection: the probe is a learned linear map of the
+ * layer input, rho = W_R x (news.chathome.org article, "What is Parallax";
+ * gist.science summary, "Method: Parallax / core mechanism"), computed as one
+ * more block of output features of the q/k/v projection.  No bias.
+ *
+ *   x   : device, [B, T, d_model] bf16 (tokens row-major)
+ *   w   : device, [(2 Hq + 2 Hkv) d, d_model] bf16, one row per output
+ *         feature (a torch Linear weight): rows 0 .. Hq d - 1 are q (feature
+ *         h d + a is dim a of query head h), then Hkv d rows of k, Hkv d rows
+ *         of v, Hq d rows of rho.
+ *   q, rho : device, [B, Hq, T, d] bf16 outputs;  k, v : [B, Hkv, T, d].
+ *
+ * Each output element is sum_c w[f][c] x[t][c] accumulated in fp32 and
+ * rounded once to bf16 (RNE).  Supported: bf16, d in {64, 128}, d_model a
+ * multiple of 64.  Returns PLX_ERR_INVALID_ARGUMENT for null or misaligned
+ * pointers, non-positive sizes, or an output overlapping an input or another
+ * output; PLX_ERR_UNSUPPORTED for other dtypes, d or d_model.
+ */
+plx_status_t parallax_qkvr_projection(const void *x, const void *w, void *q,
+                                      void *k, void *v, void *rho, int32_t B,
+                                      int32_t T, int32_t d_model, int32_t Hq,
+                                      int32_t Hkv, int32_t d,
+                                      plx_dtype_t dtype, plx_stream_t stream);
+
+/*
  * Bytes of device workspace parallax_fwd_decode needs for these sizes and
  * this split setting (keys_per_split as passed to parallax_fwd_decode; 0 =
  * the library's own choice).  Returns 0 when the call needs no workspace

@@ -7,7 +7,7 @@ seeded synthetic inputs.  PyTorch supplies device memory and streams only.
 """
 from ._native import EXPORTS, LIB_PATH, ParallaxError, load as load_library
 from .api import (ParallaxAttention, decode, decode_auto_split, decode_workspace_size, prefill,
-                  prefill_backward, prefill_train)
+                  prefill_backward, prefill_train, qkvr_projection)
 
-__all__ = ["prefill", "prefill_train", "prefill_backward", "ParallaxAttention", "decode",
+__all__ = ["prefill", "prefill_train", "prefill_backward", "ParallaxAttention", "qkvr_projection", "decode",
            "decode_workspace_size", "decode_auto_split", "ParallaxError", "LIB_PATH", "EXPORTS", "load_library"]

@@ -25,6 +25,7 @@ EXPORTS = (
     "parallax_fwd_prefill_train",
     "parallax_bwd_prefill_workspace_size",
     "parallax_bwd_prefill",
+    "parallax_qkvr_projection",
     "parallax_fwd_decode_workspace_size",
     "parallax_fwd_decode",
     "parallax_fwd_decode_auto_split",
@@ -63,6 +64,8 @@ def load():
     lib.parallax_bwd_prefill.argtypes = [vp] * 13 + [i32, i32, i32, i32, i32, f32, ctypes.c_int, vp,
                                                      ctypes.c_size_t, vp]
     lib.parallax_bwd_prefill.restype = ctypes.c_int
+    lib.parallax_qkvr_projection.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_int, vp]
+    lib.parallax_qkvr_projection.restype = ctypes.c_int
     lib.parallax_fwd_decode_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int, i32]
     lib.parallax_fwd_decode_workspace_size.restype = ctypes.c_size_t
     lib.parallax_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32, ctypes.c_int,

@@ -151,6 +151,27 @@ class ParallaxAttention(torch.autograd.Function):
         return dq, dk, dv, drho, None
 
 
+def qkvr_projection(x: torch.Tensor, w: torch.Tensor, Hq: int, Hkv: int, d: int, *, stream=None):
+    """Fused q/k/v/probe projection.  x: [B, T, d_model]; w: [(2 Hq + 2 Hkv) d,
+    d_model] (q, k, v, probe rows).  Returns (q, k, v, rho) in the attention
+    layout [B, H, T, d] (bf16)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, d_model]")
+    B, T, dm = x.shape
+    if w.shape != ((2 * Hq + 2 * Hkv) * d, dm):
+        raise ValueError("w must be [(2 Hq + 2 Hkv) d, d_model]")
+    _check_tensors(x.dtype, x=x, w=w)
+    code = _dtype_code(x.dtype)
+    q = torch.empty((B, Hq, T, d), dtype=x.dtype, device=x.device)
+    k = torch.empty((B, Hkv, T, d), dtype=x.dtype, device=x.device)
+    v = torch.empty_like(k)
+    rho = torch.empty_like(q)
+    st = N.load().parallax_qkvr_projection(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), _ptr(rho), B, T, dm, Hq,
+                                           Hkv, d, code, _stream(stream))
+    N.check(st, "parallax_qkvr_projection")
+    return q, k, v, rho
+
+
 def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype=torch.bfloat16,
                           keys_per_split: int = 0) -> int:
     n = N.load().parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype),

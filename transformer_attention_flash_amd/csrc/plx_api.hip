@@ -236,6 +236,58 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v, c
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
+plx_status_t parallax_qkvr_projection(const void *x, const void *w, void *q, void *k, void *v, void *rho,
+                                      int32_t B, int32_t T, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t d,
+                                      plx_dtype_t dtype, plx_stream_t stream) {
+    if (!x || !w || !q || !k || !v || !rho) return PLX_ERR_INVALID_ARGUMENT;
+    const void *ptrs[] = {x, w, q, k, v, rho};
+    for (const void *ptr : ptrs)
+        if (!aligned16(ptr)) return PLX_ERR_INVALID_ARGUMENT;
+    if (B < 1 || T < 1 || d_model < 1 || Hq < 1 || Hkv < 1 || d < 1) return PLX_ERR_INVALID_ARGUMENT;
+    if (dtype != PLX_DTYPE_BF16 && dtype != PLX_DTYPE_F32) return PLX_ERR_UNSUPPORTED;
+    if (dtype != PLX_DTYPE_BF16 || !supported_dim(d) || d_model % plx::projection_step() != 0)
+        return PLX_ERR_UNSUPPORTED;
+    const int64_t n_tokens = static_cast<int64_t>(B) * T;
+    const int64_t features = (2 * static_cast<int64_t>(Hq) + 2 * Hkv) * d;
+    const int64_t n_fblk = (features + plx::projection_block_features() - 1) / plx::projection_block_features();
+    const int64_t n_tblk = (n_tokens + plx::projection_block_tokens() - 1) / plx::projection_block_tokens();
+    if (n_fblk * n_tblk > kMaxGrid || features > (int64_t{1} << 30)) return PLX_ERR_UNSUPPORTED;
+
+    const size_t xb = static_cast<size_t>(n_tokens) * d_model * 2;
+    const size_t wb = static_cast<size_t>(features) * d_model * 2;
+    const size_t qb = static_cast<size_t>(n_tokens) * Hq * d * 2;
+    const size_t kb = static_cast<size_t>(n_tokens) * Hkv * d * 2;
+    struct Span { const void *p; size_t n; };
+    const Span ins[] = {{x, xb}, {w, wb}};
+    const Span outs[] = {{q, qb}, {k, kb}, {v, kb}, {rho, qb}};
+    for (const Span &o : outs) {
+        for (const Span &in : ins)
+            if (overlaps(o.p, o.n, in.p, in.n)) return PLX_ERR_INVALID_ARGUMENT;
+        for (const Span &other : outs)
+            if (&other != &o && overlaps(o.p, o.n, other.p, other.n)) return PLX_ERR_INVALID_ARGUMENT;
+    }
+
+    plx::ProjectionParams p;
+    p.x = x;
+    p.w = w;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.rho = rho;
+    p.n_tokens = n_tokens;
+    p.T = T;
+    p.d_model = d_model;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.nq = Hq * d;
+    p.nkv = Hkv * d;
+    p.n_fblk = static_cast<int32_t>(n_fblk);
+    p.n_tblk = static_cast<int32_t>(n_tblk);
+    const hipError_t e = plx::launch_projection(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
 size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx,
                                           plx_dtype_t dtype, int32_t keys_per_split) {
     DecodePlan plan;

@@ -52,6 +52,16 @@ struct BackwardParams {
     float scale_log2;              // softmax scale * log2(e)
 };
 
+struct ProjectionParams {
+    const void *x;                 // [n_tokens, d_model] (tokens = B x T, row-major)
+    const void *w;                 // [(2 Hq + 2 Hkv) d, d_model]: q, k, v, probe rows
+    void *q, *k, *v, *rho;         // [B, Hq | Hkv, T, d]
+    int64_t n_tokens;
+    int32_t T, d_model, Hq, Hkv, d;
+    int32_t nq, nkv;               // Hq d, Hkv d
+    int32_t n_fblk, n_tblk;        // feature and token blocks
+};
+
 // Both return the first launch error (hipSuccess when everything queued).
 hipError_t launch_decode(const DecodeParams &p, bool bf16, int D, int G, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, bool bf16, int D, int G, bool has_rho,
@@ -64,5 +74,11 @@ int prefill_block_positions(bool bf16, int G);
 hipError_t launch_backward(const BackwardParams &p, int D, int G, hipStream_t stream);
 int backward_q_block_positions(int G);
 int backward_k_block_keys();
+
+// Fused q/k/v/probe projection (bf16).
+hipError_t launch_projection(const ProjectionParams &p, hipStream_t stream);
+int projection_block_features();
+int projection_block_tokens();
+int projection_step();
 
 }  // namespace plx

@@ -84,6 +84,17 @@ def make_prefill(B, Hq, Hkv, T, d, dtype, device, seed: int = 0, rho_std: float 
     return out
 
 
+def make_projection(B, T, d_model, Hq, Hkv, d, dtype, device, seed: int = 0):
+    """Layer input x [B, T, d_model] ~ N(0, 1) and a stacked q/k/v/probe
+    weight [(2 Hq + 2 Hkv) d, d_model] ~ N(0, 1/d_model), so projected
+    features have unit variance."""
+    g = _generator(device, 2000 + seed)
+    x = _fill_normal(torch.empty((B, T, d_model), dtype=dtype, device=device), g)
+    w = _fill_normal(torch.empty(((2 * Hq + 2 * Hkv) * d, d_model), dtype=dtype, device=device), g,
+                     1.0 / d_model ** 0.5)
+    return x, w
+
+
 def make_upstream_grad(shape, dtype, device, seed: int = 0):
     """An upstream gradient dO ~ N(0, 1) (the backward's second input), drawn
     from its own generator seeded with 1000 + seed so it does not disturb the
