@@ -47,12 +47,12 @@ template <int CH>
 __device__ __forceinline__ VChunk<BF16, CH> vchunk_load(const uint16_t *p) {
     VChunk<BF16, CH> c;
     if constexpr (CH == 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));  // streamed once
 #pragma unroll
         for (int j = 0; j < 4; ++j) c.w[j] = x[j];
     } else {
         static_assert(CH == 4, "value chunk");
-        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
         c.w[0] = x[0];
         c.w[1] = x[1];
     }
@@ -63,7 +63,7 @@ __device__ __forceinline__ VChunk<F32, CH> vchunk_load(const float *p) {
     VChunk<F32, CH> c;
 #pragma unroll
     for (int j = 0; j < CH / 4; ++j) {
-        const f32x4 x = reinterpret_cast<const f32x4 *>(p)[j];
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) c.v[4 * j + e] = x[e];
     }
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NW *kWave) void decode_split_kernel(DecodeParams p)
             for (int blk = 0; blk < 2; ++blk) {
                 const int64_t key = min(kt + 16 * blk + col, last);
 #pragma unroll
-                for (int s = 0; s < KS; ++s) kop[sb][blk][s] = op8_load(kbase + key * D + 32 * s + 8 * grp);
+                for (int s = 0; s < KS; ++s) kop[sb][blk][s] = op8_load_stream(kbase + key * D + 32 * s + 8 * grp);
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
