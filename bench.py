@@ -111,9 +111,23 @@ def cpu_baseline_decode(x, w, budget_s: float):
             nseq += q.shape[0]
             done_bytes += q.shape[0] * per_seq_bytes
         passes += 1
+    # The explicit form (a d x d covariance per row, O(L d^2)) on its own,
+    # smaller sample: whole sequences until about a quarter of the budget.
+    e_bytes, e_spent, e_seq = 0, 0.0, 0
+    for q, r, k, v in chunks:
+        for i in range(q.shape[0]):
+            if e_spent >= budget_s / 4:
+                break
+            t0 = time.perf_counter()
+            oracle.decode(q[i:i + 1], r[i:i + 1], k[i:i + 1], v[i:i + 1], tau, form=oracle.EXPLICIT)
+            e_spent += time.perf_counter() - t0
+            e_seq += 1
+            e_bytes += per_seq_bytes
     return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{passes} pass(es) over all {w.B} sequences ({w.Hq} heads, {w.L} keys each; {nseq} "
-                      f"sequence evaluations), fp64 expanded form, {spent:.1f} s"}
+                      f"sequence evaluations), fp64 expanded form, {spent:.1f} s",
+            "explicit_form": {"value": e_bytes / e_spent / 1e9, "unit": "GB/s",
+                              "sample": f"{e_seq} whole sequence(s), fp64 explicit covariance form, {e_spent:.1f} s"}}
 
 
 def cpu_baseline_prefill(x, w, budget_s: float):
