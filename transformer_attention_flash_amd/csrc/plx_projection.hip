@@ -14,12 +14,10 @@
 // operand = weight rows), tokens along the columns (B operand = token rows),
 // both with the model dimension contiguous, so each lane ends up holding 4
 // consecutive head dimensions of one token and writes them with one 8-byte
-// store.  Block: 256 features x 128 tokens, 64-wide steps over d_model,
-// double-buffered in LDS; 8 wavefronts, each 64 features x 64 tokens
-// (4 x 4 tiles of v_mfma_f32_16x16x32_bf16).  The block shape is set by the
-// CU's memory pipeline: a step moves 48 KB into LDS (about 768 cycles at
-// 64 B per clock) for 1024 cycles of matrix work per SIMD; a 128 x 128 block
-// would move 32 KB for half the work and wait on loads.
+// store.  Block: 256 features x 256 tokens, 64-wide steps over d_model,
+// double-buffered in LDS (exactly the 160 KB of a CU); 8 wavefronts, each 64
+// features x 128 tokens (4 x 8 tiles of v_mfma_f32_16x16x32_bf16), so every
+// operand read from LDS feeds 4 or 8 MFMAs.
 #include "plx_device.h"
 #include "plx_kernels.h"
 
@@ -28,7 +26,7 @@ namespace plx {
 namespace {
 
 constexpr int kPF = 256;        // features per block
-constexpr int kPT = 128;        // tokens per block
+constexpr int kPT = 256;        // tokens per block
 constexpr int kPK = 64;         // model-dimension step
 constexpr int kPRS = kPK + 16;  // LDS row stride (elements): 160-byte rows; measured against 144, 176 and 192 bytes, 4% faster
 constexpr int kPWaves = 8;
@@ -45,7 +43,7 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
     const int wave = tid / kWave;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int wf = wave & 3, wt = wave >> 2;  // wavefront's 64 x 64 tile of the block
+    const int wf = wave & 3, wt = wave >> 2;  // wavefront's 64-feature x 128-token tile of the block
 
     // Block order: workgroups are dealt to the 8 XCDs round-robin.  Within an
     // XCD, blocks run in groups of kGroupT token blocks, feature block outer,
@@ -109,11 +107,12 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
         for (int n = 0; n < NXC; ++n) store_op8(&lds_x[buf][xl[n]], sx[n]);
     };
 
-    f32x4 acc[4][4];
+    constexpr int NI = 4, NJ = 8;  // 16 x 16 tiles per wavefront: features x tokens
+    f32x4 acc[NI][NJ];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NI; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NJ; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int n_steps = K / kPK;
     load(0);
@@ -123,34 +122,33 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
         __syncthreads();
         const bool more = s + 1 < n_steps;
         if (more) load((s + 1) * kPK);
-        const S *tw = lds_w[buf] + (64 * wf) * kPRS;
-        const S *tx = lds_x[buf] + (64 * wt) * kPRS;
+        const S *tw = lds_w[buf] + (16 * NI * wf) * kPRS;
+        const S *tx = lds_x[buf] + (16 * NJ * wt) * kPRS;
 #pragma unroll
         for (int ks = 0; ks < kPK / 32; ++ks) {
-            Op8<BF16> a[4], b[4];
+            Op8<BF16> a[NI], b[NJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = op8_load(tw + (16 * i + col) * kPRS + 32 * ks + 8 * grp);
-                b[i] = op8_load(tx + (16 * i + col) * kPRS + 32 * ks + 8 * grp);
-            }
+            for (int i = 0; i < NI; ++i) a[i] = op8_load(tw + (16 * i + col) * kPRS + 32 * ks + 8 * grp);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < NJ; ++j) b[j] = op8_load(tx + (16 * j + col) * kPRS + 32 * ks + 8 * grp);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mma32(a[i], b[j], acc[i][j]);
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mma32(a[i], b[j], acc[i][j]);
         }
         if (more) store(buf ^ 1);
     }
 
     // acc[i][j][e] is feature f0 + 64 wf + 16 i + 4 grp + e of token
-    // t0 + 64 wt + 16 j + col.  Four consecutive features share a head.
+    // t0 + 128 wt + 16 j + col.  Four consecutive features share a head.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + 64 * wt + 16 * j + col;
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t t = t0 + 16 * NJ * wt + 16 * j + col;
         if (t >= M) continue;
         const int64_t bb = t / p.T, tt = t % p.T;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int f = f0 + 64 * wf + 16 * i + 4 * grp;
+        for (int i = 0; i < NI; ++i) {
+            int f = f0 + 16 * NI * wf + 16 * i + 4 * grp;
             if (f >= n_feat) continue;
             void *base;
             int H;
