@@ -189,6 +189,54 @@ def cpu_baseline_backward(x, dout, w):
                       f"closed-form fp64 gradients with numpy, {dt:.1f} s"}
 
 
+def measure_device(torch):
+    """The device's own ceilings beside the datasheet figures: the bf16 MFMA
+    peak implied by its compute units and maximum clock, and measured rates of
+    a plain streaming read (cached and non-temporal 16-byte loads over 2 GiB,
+    far beyond the caches) and of a kernel doing nothing but bf16 MFMAs at
+    two wavefronts per SIMD."""
+    from transformer_attention_flash_amd import diag
+
+    info = diag.device_info()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def best_seconds(fn, reps, rounds=3):
+        best = None
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / reps
+            best = t if best is None or t < best else best
+        return best
+
+    measured = {}
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    for nt in (False, True):
+        fn = lambda: diag.stream_read(buf, nontemporal=nt, sink=sink)  # noqa: E731
+        for _ in range(3):
+            fn()
+        key = "stream_read_nontemporal_GBs" if nt else "stream_read_cached_GBs"
+        measured[key] = round(nbytes / best_seconds(fn, 10) / 1e9, 1)
+    del buf
+    n_blocks, iters = 2 * info["compute_units"], 16000
+    flops = n_blocks * 4 * 8 * iters * diag.MFMA_FLOP
+    fn = lambda: diag.mfma_bf16(n_blocks, iters, sink=sink)  # noqa: E731
+    for _ in range(20):  # ~40 ms: lets the clock settle under matrix load
+        fn()
+    measured["bf16_mfma_tflops"] = round(flops / best_seconds(fn, 10) / 1e12, 1)
+    torch.cuda.synchronize()
+    return {"name": torch.cuda.get_device_properties(0).gcnArchName,
+            "compute_units": info["compute_units"], "max_clock_mhz": info["max_clock_mhz"],
+            "bf16_mfma_peak_tflops_from_clock": round(info["bf16_mfma_peak_tflops"], 1),
+            "datasheet": {"hbm_GBs": HBM_PEAK_GBS, "bf16_mfma_tflops": BF16_MFMA_PEAK_TFLOPS},
+            "measured": measured}
+
+
 def run_sweep(args, torch, plx, synth):
     """Decode sweep, Parallax against the softmax-only path (rho = NULL) of the
     same library: batch x context over the pages' range (batch 1..2048,
@@ -197,7 +245,9 @@ def run_sweep(args, torch, plx, synth):
       compute-matched: Parallax at d = 64 against softmax-only at d = 128
                        (equal matrix flops per key: Parallax has two scoring
                        and two value products, softmax attention one each).
-    Prints one JSON line per grid point."""
+    Points whose eager call takes under 50 us are also timed as 64 calls
+    replayed from one HIP graph (the *_graph_* fields).  Prints one JSON line
+    per grid point."""
     dev = "cuda"
     grid = [(b, l) for b in (1, 16, 128, 1024, 2048) for l in (128, 1024, 8192, 32768) if b * l <= 1 << 23]
 
@@ -218,6 +268,36 @@ def run_sweep(args, torch, plx, synth):
             best = t if best is None or t < best else best
         return best
 
+    def graph_timed(fn, n_calls=64):
+        # n_calls calls captured in one HIP graph and replayed: the per-call
+        # time without the host's launch overhead, which dominates small
+        # decode steps launched one by one.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n_calls):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / (5 * n_calls) * 1e3
+            best = t if best is None or t < best else best
+        del g
+        return best
+
     for B, L in grid:
         row = {"B": B, "context": L}
         for name, d, with_rho in (("parallax_d128", 128, True), ("softmax_d128", 128, False),
@@ -225,11 +305,20 @@ def run_sweep(args, torch, plx, synth):
             x = synth.make_decode(B, 16, 8, L, d, torch.bfloat16, dev, seed=0)
             out = torch.empty_like(x["q"])
             rho = x["rho"] if with_rho else None
+            ws = torch.empty(max(plx.decode_workspace_size(B, 16, 8, d, L), 1), dtype=torch.uint8, device=dev)
             nbytes = 4 * B * 8 * L * d
-            us = timed(lambda: plx.decode(x["q"], x["k"], x["v"], rho, out=out), nbytes)
+
+            def call():
+                plx.decode(x["q"], x["k"], x["v"], rho, out=out, workspace=ws)
+
+            us = timed(call, nbytes)
             row[name + "_us"] = round(us, 2)
             row[name + "_GBs"] = round(nbytes / us / 1e3, 1)
-            del x, out
+            if us < 50:  # launch-bound sizes: also replayed from a graph
+                gus = graph_timed(call)
+                row[name + "_graph_us"] = round(gus, 2)
+                row[name + "_graph_GBs"] = round(nbytes / gus / 1e3, 1)
+            del x, out, ws
         torch.cuda.empty_cache()
         row["io_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d128_us"], 3)
         row["compute_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d64_us"], 3)
@@ -251,6 +340,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-projection", action="store_true")
+    ap.add_argument("--no-device", action="store_true", help="skip the device ceiling measurements")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--backward-warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
@@ -458,6 +548,18 @@ def main():
             if not args.no_cpu_baseline:
                 log("backward CPU baseline (oracle)")
                 result["prefill"]["backward"]["cpu_baseline"] = cpu_baseline_backward(x, dout, pw)
+
+    if not args.no_device:
+        log("device ceilings: streaming read, MFMA-only kernel")
+        dv = measure_device(torch)
+        result["device"] = dv
+        m = dv["measured"]
+        result["roofline"]["frac_of_measured_stream_read"] = round(gbs / m["stream_read_nontemporal_GBs"], 4)
+        if "prefill" in result:
+            pr = result["prefill"]
+            for part in (pr, pr.get("projection"), pr.get("backward")):
+                if part is not None:
+                    part["roofline"]["frac_of_measured_mfma"] = round(part["value"] / m["bf16_mfma_tflops"], 4)
 
     print(json.dumps(result), flush=True)
 

@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/parallax.h declares, and every rejected call returns its status code
+the headers in include/ declare, and every rejected call returns its status code
 from the host-side checks (which run before any HIP call)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,7 +11,7 @@ import pytest
 from transformer_attention_flash_amd import _native as N
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "parallax.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 BF16, F32 = N.PLX_DTYPE_BF16, N.PLX_DTYPE_F32
 INVALID, UNSUP, WS = N.PLX_ERR_INVALID_ARGUMENT, N.PLX_ERR_UNSUPPORTED, N.PLX_ERR_WORKSPACE_TOO_SMALL
@@ -30,9 +31,11 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(parallax_\w+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(parallax_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_and_exports_agree(lib):
@@ -177,6 +180,24 @@ def test_decode_auto_split(lib):
     assert f(64, 8, 8, 128, 1 << 24) == 1 << 20     # chunk capped at 2^20 keys
     assert f(2, 6, 4, 128, 100) == -INVALID
     assert f(2, 4, 2, 100, 100) == -UNSUP
+
+
+def test_diag_rejections(lib):
+    one = ctypes.c_int32()
+    assert lib.parallax_diag_device_info(0, None, ctypes.byref(one)) == INVALID
+    assert lib.parallax_diag_device_info(0, ctypes.byref(one), None) == INVALID
+    f = lib.parallax_diag_stream_read
+    assert f(None, 1 << 20, 1, P[1], None) == INVALID
+    assert f(P[0], 1 << 20, 1, None, None) == INVALID
+    assert f(P[0], 0, 1, P[1], None) == INVALID           # empty
+    assert f(P[0], 1000, 1, P[1], None) == INVALID        # not a multiple of 16
+    assert f(P[0] + 8, 1 << 20, 1, P[1], None) == INVALID  # misaligned source
+    assert f(P[0], 1 << 20, 1, P[0] + 64, None) == INVALID  # sink inside the source
+    g = lib.parallax_diag_mfma_bf16
+    assert g(None, 512, 100, None) == INVALID
+    assert g(P[0], 0, 100, None) == INVALID
+    assert g(P[0], 512, 0, None) == INVALID
+    assert g(P[0], (1 << 20) + 1, 100, None) == INVALID
 
 
 def test_product_does_not_use_the_oracle():

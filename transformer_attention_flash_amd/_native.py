@@ -30,6 +30,9 @@ EXPORTS = (
     "parallax_fwd_decode",
     "parallax_fwd_decode_auto_split",
     "parallax_status_string",
+    "parallax_diag_device_info",
+    "parallax_diag_stream_read",
+    "parallax_diag_mfma_bf16",
 )
 
 _lib = None
@@ -75,6 +78,12 @@ def load():
     lib.parallax_fwd_decode_auto_split.restype = i32
     lib.parallax_status_string.argtypes = [ctypes.c_int]
     lib.parallax_status_string.restype = ctypes.c_char_p
+    lib.parallax_diag_device_info.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.parallax_diag_device_info.restype = ctypes.c_int
+    lib.parallax_diag_stream_read.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+    lib.parallax_diag_stream_read.restype = ctypes.c_int
+    lib.parallax_diag_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    lib.parallax_diag_mfma_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 

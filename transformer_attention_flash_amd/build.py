@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libparallax.so")
-SOURCES = ["plx_api.hip", "plx_decode.hip", "plx_prefill.hip", "plx_backward.hip", "plx_projection.hip"]
+SOURCES = ["plx_api.hip", "plx_decode.hip", "plx_prefill.hip", "plx_backward.hip", "plx_projection.hip",
+           "plx_diag.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the generated code.
