@@ -167,6 +167,58 @@ def test_prefill_rho_zero_is_bitwise_softmax_only(dtype):
     assert_close(host64(a), host64(ref), dtype, "softmax-only vs torch fp32 causal attention")
 
 
+def _assert_close_sharp(got, ref, dtype, what):
+    """Sharp weights make outputs close to single value entries (|o| up to
+    ~6 instead of the O(0.1) averages of the standard workloads), and the
+    probe terms B/l and (c/l) o^SA, which nearly cancel, are of that size too.
+    In bf16 the output rounding and the roundings of P and P*R to bf16 each
+    cost up to half an ulp of such values, so the per-element bound is
+    2^-7 |oracle| (at most two bf16 ulps) + 1.5e-2.  In fp32 the scores reach
+    ~130 in log2 units here, and the rounding of that exponent argument
+    (~2^-24 * 130 ~ 8e-6) becomes a relative error of the weights of that
+    size, so the bound is 1e-5 + 4e-6 |oracle|.  rel-L2 stays at 5e-3."""
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bound = (2.0 ** -7 * np.abs(ref) + 1.5e-2) if dtype == BF else (4e-6 * np.abs(ref) + 1e-5)
+    max_abs, rel = float(err.max()), float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst/bound={float((err / bound).max()):.3f}")
+    assert (err <= bound).all(), f"{what}: {int((err > bound).sum())} elements beyond the bound"
+    assert rel <= 5e-3, f"{what}: rel_l2 {rel:.3e}"
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_prefill_sharp_scores(dtype):
+    """Queries scaled by 8 (exact in both dtypes): scores ~ N(0, 64), so along a
+    row the running max rises past the rescale slack many times and the
+    weights span many orders of magnitude; one late key per KV head is also
+    aligned with the query rows to force a rescale well inside the row."""
+    d = 128 if dtype == BF else 64
+    say(f"prefill sharp scores {dtype}")
+    gen_dev = "cpu" if dtype == F32 else DEV
+    x = synth.make_prefill(1, 4, 2, 600, d, dtype, gen_dev, seed=8)
+    x = {k: v.to(DEV) for k, v in x.items()}
+    x["q"] = x["q"] * 8
+    x["k"][:, :, 450, :] = x["q"][:, 0::2, 450, :] / 8  # key 450 of KV head g aligned with query head 2g
+    out = plx.prefill(x["q"], x["k"], x["v"], x["rho"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["rho"]), _tau(d))
+    _assert_close_sharp(host64(out), ref, dtype, f"prefill sharp {dtype}")
+
+
+def test_decode_sharp_scores():
+    """Decode with scores ~ N(0, 64) and one late aligned key, split into chunks
+    whose maxima differ by large amounts (the merge rescales them)."""
+    say("decode sharp scores")
+    x = synth.make_decode(2, 8, 4, 3000, 128, BF, DEV, seed=9)
+    x["q"] = x["q"] * 8
+    x["k"][:, :, 2900, :] = x["q"][:, 0::2, :] / 8
+    ref = oracle.decode(host64(x["q"]), host64(x["rho"]), host64(x["k"]), host64(x["v"]), _tau(128))
+    for ks in (0, 256):
+        out = plx.decode(x["q"], x["k"], x["v"], x["rho"], keys_per_split=ks)
+        torch.cuda.synchronize()
+        _assert_close_sharp(host64(out), ref, BF, f"decode sharp ks={ks}")
+
+
 def test_prefill_deterministic():
     say("prefill determinism")
     x = synth.make_prefill(1, 16, 8, 700, 128, BF, DEV, seed=6)
