@@ -200,6 +200,21 @@ def test_diag_rejections(lib):
     assert g(P[0], (1 << 20) + 1, 100, None) == INVALID
 
 
+def test_c_caller_builds_and_rejects_bad_usage():
+    """The plain-C caller (tests/c/abi_check.c) compiles against the headers and
+    links to libparallax.so; bad command lines fail before any HIP call."""
+    import subprocess
+    import sys
+    sys.path.insert(0, ROOT)
+    import __graft_entry__
+    exe = __graft_entry__.build_c_abi_check()
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 1 and "usage" in res.stderr
+    res = subprocess.run([exe, "bogus", "/nonexistent", "1", "1", "1", "1", "64"], capture_output=True, text=True,
+                         timeout=60)
+    assert res.returncode == 1 and "mode" in res.stderr
+
+
 def test_product_does_not_use_the_oracle():
     """Only tests, the smoke check and the benchmark's CPU leg may touch oracle/."""
     pkg = os.path.join(ROOT, "transformer_attention_flash_amd")
