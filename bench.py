@@ -44,6 +44,12 @@ DECODE_SOURCES = ["transformer_attention_flash_amd/csrc/plx_decode.hip",
                   "transformer_attention_flash_amd/csrc/plx_device.h"]
 PREFILL_SOURCES = ["transformer_attention_flash_amd/csrc/plx_prefill.hip",
                    "transformer_attention_flash_amd/csrc/plx_device.h"]
+BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "backward_b8_t4096_traffic.md")
+BACKWARD_SOURCES = ["transformer_attention_flash_amd/csrc/plx_backward.hip",
+                    "transformer_attention_flash_amd/csrc/plx_device.h"]
+PROJECTION_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "projection_t32768_dm2048_traffic.md")
+PROJECTION_SOURCES = ["transformer_attention_flash_amd/csrc/plx_projection.hip",
+                      "transformer_attention_flash_amd/csrc/plx_device.h"]
 
 
 def log(*a):
@@ -499,6 +505,7 @@ def main():
             jsecs, _ = time_steps(projection_step, args.prefill_steps, args.prefill_warmup, torch)
             lsecs, _ = time_steps(library_gemm_step, args.prefill_steps, args.prefill_warmup, torch)
             jflops = 2 * pw.B * pw.T * (2 * pw.Hq + 2 * pw.Hkv) * pw.d * dm
+            jtraffic = read_traffic(source_digest(PROJECTION_SOURCES), PROJECTION_TRAFFIC_FILE)
             jtf = jflops / (jsecs / args.prefill_steps) / 1e12
             log(f"projection: {jsecs / args.prefill_steps * 1e3:.3f} ms, {jtf:.1f} TFLOP/s; library GEMM alone "
                 f"{lsecs / args.prefill_steps * 1e3:.3f} ms")
@@ -506,7 +513,8 @@ def main():
                 "value": round(jtf, 2), "unit": "TFLOP/s", "ms_per_step": round(jsecs / args.prefill_steps * 1e3, 4),
                 "shape": {"tokens": pw.B * pw.T, "d_model": dm, "features": (2 * pw.Hq + 2 * pw.Hkv) * pw.d},
                 "roofline": {"bound": "mfma", "achieved": round(jtf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(jtf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "unit": "TFLOP/s", "frac": round(jtf / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": jtraffic if jtraffic is None else round(jtraffic),
                              "kernel": "projection_kernel (one parallax_qkvr_projection call)"},
                 "context_library_gemm_ms": round(lsecs / args.prefill_steps * 1e3, 4),
             }
@@ -532,6 +540,7 @@ def main():
             # dRho); the kernels execute 11, since dq and dk/dv each recompute
             # S, R and g.
             bflops = 8 * 2 * pw.d * pairs
+            btraffic = read_traffic(source_digest(BACKWARD_SOURCES), BACKWARD_TRAFFIC_FILE)
             btf = bflops / (bsecs / args.backward_steps) / 1e12
             log(f"backward: {bsecs / args.backward_steps * 1e3:.3f} ms/step, {btf:.1f} TFLOP/s; training forward "
                 f"{fsecs / args.backward_steps * 1e3:.3f} ms")
@@ -541,7 +550,8 @@ def main():
                 "us_per_step_median": round(sorted(bper)[len(bper) // 2] * 1e3, 2),
                 "algorithmic_flops_per_step": bflops, "executed_gemm_equivalents": 11,
                 "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(btf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "unit": "TFLOP/s", "frac": round(btf / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": btraffic if btraffic is None else round(btraffic),
                              "kernel": "bwd_rowstat + bwd_dq + bwd_dkdv (one parallax_bwd_prefill call)"},
                 "training_forward_ms": round(fsecs / args.backward_steps * 1e3, 4),
             }
