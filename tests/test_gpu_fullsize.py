@@ -103,3 +103,25 @@ def test_prefill_full_size():
     b = plx.prefill(x["q"], x["k"], x["v"], None)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_prefill_beyond_2_31_elements():
+    """q, rho and out of 72 x 16 x 16384 x 128 = 2.4e9 elements each: the last
+    sequence's rows start at element 71 * 2^25 > 2^31, so every offset must
+    be 64-bit.  Sampled rows of the first and last sequences and of three
+    heads, at the first, last and block-edge positions, against the oracle."""
+    B, Hq, Hkv, T, d = 72, 16, 8, 16384, 128
+    say(f"prefill past 2^31 elements: B={B} Hq={Hq} Hkv={Hkv} T={T} d={d} ({B * Hq * T * d} elements per q)")
+    x = synth.make_prefill(B, Hq, Hkv, T, d, torch.bfloat16, DEV, seed=21)
+    out = plx.prefill(x["q"], x["k"], x["v"], x["rho"])
+    torch.cuda.synchronize()
+    bs = [0, B - 1]
+    heads = [0, 5, Hq - 1]
+    ts = [0, 1, 63, 64, 4095, 8191, 8192, T - 65, T - 1]
+    sub = {n: x[n][bs] for n in ("q", "k", "v", "rho")}
+    rows = np.array([(i, h, t) for i in range(len(bs)) for h in heads for t in ts], dtype=np.int64)
+    ref = oracle.prefill(host64(sub["q"]), host64(sub["k"]), host64(sub["v"]), host64(sub["rho"]), 1 / np.sqrt(d),
+                         rows=rows)
+    got = host64(out[bs])[rows[:, 0], rows[:, 1], rows[:, 2]]
+    del x, out, sub
+    assert_close(got, ref, torch.bfloat16, f"prefill past 2^31: {len(rows)} rows")
