@@ -71,3 +71,26 @@ def test_projection_full_size_sampled_tokens():
     for name, got, ref in zip(("q", "k", "v", "rho"), outs, refs):
         g = got[torch.tensor(bs), :, torch.tensor(ts)]               # [96, H, d]
         _check(g[:, :, None, :], ref, name)
+
+
+def test_projection_beyond_2_31_elements():
+    """B=2, T=540000 tokens, d_model=2048, Hq=16, Hkv=8, d=128: q and rho hold
+    2.2e9 elements each, so the last tokens' outputs sit past element 2^31
+    (64-bit output offsets); sampled tokens at both ends against the oracle."""
+    import transformer_attention_flash_amd as plx
+    from transformer_attention_flash_amd import synth
+    from oracle import projection as oproj
+    B, T, dm, Hq, Hkv, d = 2, 540000, 2048, 16, 8, 128
+    say(f"projection past 2^31 elements: B={B} T={T} ({B * T * Hq * d} elements per q)")
+    x, w = synth.make_projection(B, T, dm, Hq, Hkv, d, torch.bfloat16, "cuda")
+    outs = plx.qkvr_projection(x, w, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    bs = np.array([0, 0, 1, 1, 1, 1])
+    ts = np.array([0, T - 1, 0, 255, T - 256, T - 1])
+    xs = host64(x[torch.tensor(bs), torch.tensor(ts)])[:, None, :]
+    refs = oproj.project(xs, host64(w), Hq, Hkv, d)
+    for name, got, ref in zip(("q", "k", "v", "rho"), outs, refs):
+        g = got[torch.tensor(bs), :, torch.tensor(ts)]
+        _check(g[:, :, None, :], ref, name)
+    del x, w, outs
+    torch.cuda.empty_cache()
