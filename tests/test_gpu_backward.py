@@ -156,3 +156,35 @@ def test_backward_full_size_sampled_group_and_invariants():
     say(f"  sum_j dv_j vs sum dO: rel {rel_v:.3e}; |sum_j dk_j| / sum_j |dk_j|: {rel_k:.3e}")
     assert rel_v <= 1e-2
     assert rel_k <= 1e-2
+
+
+def test_backward_beyond_2_31_elements():
+    """B=1100, Hq=16, Hkv=8, T=1024, d=128 with a probe: q, rho, dO, o, o^SA,
+    dq and drho hold 2.3e9 elements each, so the last sequences sit past
+    element 2^31 (64-bit offsets in every backward kernel).  The last
+    sequence's last KV-head group against the oracle, plus the two gradient
+    invariants on that sequence."""
+    from oracle import grad as ograd
+    B, Hq, Hkv, T, d = 1100, 16, 8, 1024, 128
+    say(f"backward past 2^31 elements: B={B} Hq={Hq} Hkv={Hkv} T={T} d={d} ({B * Hq * T * d} elements per q)")
+    x = _inputs(B, Hq, Hkv, T, d, True, seed=3)
+    scale = 1.0 / math.sqrt(d)
+    _, (dq, dk, dv, drho) = _run(x, scale)
+    b, g = B - 1, Hkv - 1
+    G = Hq // Hkv
+    hs = slice(g * G, (g + 1) * G)
+    h = {n: host64(x[n][b:b + 1, hs] if n in ("q", "rho", "dout") else x[n][b:b + 1, g:g + 1]) for n in x}
+    ref = ograd.grad_expanded(h["q"], h["k"], h["v"], h["rho"], h["dout"], scale, groups=[(0, 0)])[(0, 0)]
+    _check_grad(dq[b, hs], ref[0], f"dq (b={b}, kv head {g})")
+    _check_grad(dk[b, g], ref[1], f"dk (b={b}, kv head {g})")
+    _check_grad(dv[b, g], ref[2], f"dv (b={b}, kv head {g})")
+    _check_grad(drho[b, hs], ref[3], f"drho (b={b}, kv head {g})")
+    dsum = x["dout"][b].double().reshape(Hkv, G, T, d).sum(dim=(1, 2))
+    vsum = dv[b].double().sum(dim=1)
+    rel_v = float((vsum - dsum).norm() / dsum.norm())
+    rel_k = float(dk[b].double().sum(dim=1).norm() / dk[b].double().abs().sum(dim=1).norm())
+    say(f"  last sequence: sum_j dv_j vs sum dO rel {rel_v:.3e}; |sum_j dk_j| / sum_j |dk_j| {rel_k:.3e}")
+    del x, dq, dk, dv, drho
+    torch.cuda.empty_cache()
+    assert rel_v <= 1e-2
+    assert rel_k <= 1e-2
