@@ -17,7 +17,7 @@
  *   section "How does the mechanism work?", fix the boundary-amplification
  *   factor eta_i to zero, so no other term appears.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - Sigma^(i)_KV is weighted by query i's softmax weights p_ij (the (i)
  *     superscript makes it query dependent); population form, the weights
  *     sum to one, no Bessel correction.
