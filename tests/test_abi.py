@@ -48,6 +48,15 @@ def test_header_and_exports_agree(lib):
         assert hasattr(lib, name)
 
 
+def test_every_kernel_stub_is_defined(lib):
+    """Every kernel the library launches has its host-side stub defined in the
+    library itself (a device-only builtin called straight from a kernel
+    template once made the host pass drop stubs silently; the library then
+    failed to load on the GPU)."""
+    out = os.popen(f"nm --undefined-only {N.LIB_PATH}").read()
+    assert "device_stub" not in out, [l for l in out.splitlines() if "device_stub" in l][:5]
+
+
 def test_status_strings(lib):
     for code in range(5):
         assert N.status_string(code)
