@@ -66,27 +66,29 @@ def test_decode_contiguous(case):
 
 
 RAGGED_CASES = [
-    # lengths, Hq, Hkv, d, keys_per_split
-    ([0, 1, 31, 32, 33, 257, 1000], 4, 2, 64, 0),
-    ([0, 1, 31, 32, 33, 257, 1000], 4, 2, 128, 64),
-    ([700, 5, 0, 0, 129], 8, 4, 128, 32),
-    ([64, 3000, 17], 16, 2, 64, 0),
+    # lengths, Hq, Hkv, d, keys_per_split, dtype
+    ([0, 1, 31, 32, 33, 257, 1000], 4, 2, 64, 0, BF),
+    ([0, 1, 31, 32, 33, 257, 1000], 4, 2, 128, 64, BF),
+    ([700, 5, 0, 0, 129], 8, 4, 128, 32, BF),
+    ([64, 3000, 17], 16, 2, 64, 0, BF),
+    ([0, 3, 200, 777], 8, 2, 128, 0, F32),
+    ([1, 129, 64], 4, 4, 64, 32, F32),
 ]
 
 
 @pytest.mark.parametrize("case", RAGGED_CASES, ids=[f"r{i}" for i in range(len(RAGGED_CASES))])
 def test_decode_ragged(case):
-    lengths, Hq, Hkv, d, ks = case
+    lengths, Hq, Hkv, d, ks, dtype = case
     say(f"decode ragged {case}")
     lens = torch.tensor(lengths, dtype=torch.int64)
-    x = synth.make_decode_ragged(lens, Hq, Hkv, d, BF, DEV, seed=2)
+    x = synth.make_decode_ragged(lens, Hq, Hkv, d, dtype, DEV, seed=2)
     out = plx.decode(x["q"], x["k"], x["v"], x["rho"], cu_seqlens=x["cu_seqlens"], max_ctx=x["max_ctx"],
                      num_kv_heads=Hkv, keys_per_split=ks)
     torch.cuda.synchronize()
     ref = oracle.decode(host64(x["q"]), host64(x["rho"]), host64(x["k"]), host64(x["v"]), _tau(d),
                         cu_seqlens=x["cu_host"].numpy(), Hkv=Hkv)
     got = host64(out)
-    assert_close(got, ref, BF, f"ragged {case}")
+    assert_close(got, ref, dtype, f"ragged {case}")
     for b, n in enumerate(lengths):
         if n == 0:
             assert (got[b] == 0).all(), "an empty sequence must give zeros"
