@@ -107,11 +107,20 @@ def prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout, *, scale: Optio
     """Gradients (dq, dk, dv, drho) of sum(dout * out) for the causal Parallax
     prefill, from the tensors prefill_train returned (bf16).  drho is None
     when rho is."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D [B, H, T, d]")
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
-    for name, t in (("out", out), ("dout", dout)):
-        if t.shape != q.shape:
+    if k.shape != (B, Hkv, T, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, T, d] matching q")
+    for name, t in (("out", out), ("dout", dout), ("rho", rho), ("out_sa", out_sa)):
+        if t is not None and t.shape != q.shape:
             raise ValueError(f"{name} must have q's shape")
+    for name, t in (("lse", lse), ("rbar", rbar)):
+        if t is not None and t.shape != (B, Hq, T):
+            raise ValueError(f"{name} must be [B, Hq, T]")
+    if lse is None:
+        raise ValueError("lse is required")
     _check_tensors(q.dtype, q=q, k=k, v=v, rho=rho, out=out, out_sa=out_sa, dout=dout)
     _check_tensors(torch.float32, lse=lse, rbar=rbar)
     code = _dtype_code(q.dtype)
@@ -119,6 +128,8 @@ def prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout, *, scale: Optio
     need = lib.parallax_bwd_prefill_workspace_size(B, Hq, T)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -126,8 +137,8 @@ def prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout, *, scale: Optio
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib.parallax_bwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out), _ptr(out_sa), _ptr(lse),
                                   _ptr(rbar), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drho),
-                                  B, Hq, Hkv, T, d, scale, code, _ptr(workspace), workspace.numel(),
-                                  _stream(stream))
+                                  B, Hq, Hkv, T, d, scale, code, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
     N.check(st, "parallax_bwd_prefill")
     return dq, dk, dv, drho
 
@@ -223,12 +234,16 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: O
         raise ValueError("rho must have q's shape")
     if out is None:
         out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
     _check_tensors(q.dtype, q=q, rho=rho, k_cache=k_cache, v_cache=v_cache, out=out)
     code = _dtype_code(q.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = decode_workspace_size(B, Hq, Hkv, d, max_ctx, q.dtype, keys_per_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = N.load().parallax_fwd_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
                                       int(max_ctx), _ptr(out), B, Hq, Hkv, d, scale, code, int(keys_per_split),
