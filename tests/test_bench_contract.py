@@ -1,0 +1,42 @@
+"""bench.py's host-side pieces, without a GPU: the committed counter
+summaries parse, and each was taken on the kernel sources as they are now
+(otherwise bench.py reports traffic as null, as it should, and the summary
+needs a new counter run)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+SUMMARIES = [
+    (bench.TRAFFIC_FILE, bench.DECODE_SOURCES),
+    (bench.PREFILL_TRAFFIC_FILE, bench.PREFILL_SOURCES),
+    (bench.BACKWARD_TRAFFIC_FILE, bench.BACKWARD_SOURCES),
+    (bench.PROJECTION_TRAFFIC_FILE, bench.PROJECTION_SOURCES),
+]
+
+
+@pytest.mark.parametrize("path,sources", SUMMARIES, ids=[os.path.basename(s[0]) for s in SUMMARIES])
+def test_traffic_summary_matches_current_sources(path, sources):
+    assert os.path.exists(path), path
+    traffic = bench.read_traffic(bench.source_digest(sources), path)
+    assert traffic is not None, f"{os.path.basename(path)} was taken on other kernel sources"
+    assert traffic > 0
+
+
+def test_read_traffic_rejects_other_sources(tmp_path):
+    p = tmp_path / "t.md"
+    p.write_text("kernel_source_digest: 0123456789abcdef\nfetch_bytes_per_launch: 1.5e9\nwrite_bytes_per_launch: 2e8\n")
+    assert bench.read_traffic("0123456789abcdef", str(p)) == pytest.approx(1.7e9)
+    assert bench.read_traffic("fedcba9876543210", str(p)) is None
+    assert bench.read_traffic("0123456789abcdef", str(tmp_path / "missing.md")) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
