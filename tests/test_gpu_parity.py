@@ -136,6 +136,9 @@ PREFILL_CASES = [
     (1, 4, 2, 100, 128, F32),
     (2, 2, 1, 1, 64, BF),            # T = 1
     (1, 2, 1, 513, 128, BF),
+    (1, 8, 2, 150, 128, F32),        # fp32, G = 4
+    (1, 16, 2, 77, 64, F32),         # fp32, G = 8
+    (2, 8, 8, 3, 64, F32),           # fp32, T < one key tile
 ]
 
 
