@@ -1,9 +1,11 @@
 // plx_decode.hip -- Parallax attention decode on gfx950: split-KV kernel and
 // the kernel that merges the splits.
 //
-// One wavefront owns one (sequence b, KV head g, key chunk) work item.  The G
-// query heads that share KV head g and their G probes form the 2G columns of
-// a 16-column MFMA tile: columns 0..G-1 are the query rows, columns G..2G-1
+// One workgroup of 1, 2, 4 or 8 wavefronts owns one (sequence b, KV head g,
+// key chunk) work item; its wavefronts take interleaved 32-key tiles of the
+// chunk and merge their states in LDS at the end.  The G query heads that
+// share KV head g and their G probes form the 2G columns of a 16-column MFMA
+// tile: columns 0..G-1 are the query rows, columns G..2G-1
 // the probe rows, the rest are zero.  One MFMA over a 16-key block of K
 // therefore gives the softmax scores S = tau q.k and the probe scores
 // R = rho.k together, and one MFMA over 32 keys of V gives the softmax

@@ -1,11 +1,11 @@
 // plx_prefill.hip -- causal Parallax attention prefill on gfx950.
 //
-// A workgroup of 4 wavefronts owns one (sequence b, KV head g, query block)
+// A workgroup of 8 wavefronts owns one (sequence b, KV head g, query block)
 // tile: 128 query rows = the G query heads that share KV head g at 128/G
-// consecutive positions.  Each wavefront owns 32 of those rows as two
-// 16-column MFMA tiles.  K/V tiles of KT keys are staged once in LDS
-// (double-buffered) and shared by every row of the workgroup and by both
-// scoring branches (the news.chathome.org article on Parallax, "Hardware
+// consecutive positions.  Each wavefront owns 16 of those rows as one
+// 16-column MFMA tile.  K/V tiles of KT keys are staged once in LDS (two
+// or, for bf16 with the probe, four buffers) and shared by every row of the
+// workgroup and by both scoring branches (the news.chathome.org article on Parallax, "Hardware
 // argument": the two branches share the online max, the scaling factors and
 // the K and V tiles; the gist.science summary, "Hardware-aware algorithm").
 //
