@@ -35,6 +35,7 @@ namespace plx {
 namespace {
 
 constexpr float kRescaleSlack = 8.f;
+constexpr int kCombineWaves = 4;  // wavefronts merging one (sequence, query head) row
 
 // The d/16 head-dimension elements a lane reads from one value row.
 template <class T, int CH> struct VChunk;
@@ -359,30 +360,48 @@ __global__ __launch_bounds__(NW *kWave) void decode_split_kernel(DecodeParams p)
 // then (l, c, A, B) = sum_s w_s (l_s, c_s, A_s, B_s) in chunk order, and the
 // same epilogue as the single-chunk path.
 template <class T, int D>
-__global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombineWaves *kWave) void decode_combine_kernel(DecodeParams p) {
     using S = typename T::storage;
     constexpr int PER = D / kWave;  // head-dim elements per lane
-    const int lane = threadIdx.x;
+    constexpr int NW = kCombineWaves;
+    __shared__ float s_red[NW][2 + 2 * D];  // per wavefront: l, c, A[D], B[D]
+    __shared__ float s_max[NW];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
     const int64_t row = blockIdx.x;
     const int b = static_cast<int>(row / p.Hq);
     S *o = static_cast<S *>(p.out) + row * D;
 
     const SeqView sv = seq_view(p, b);
     if (sv.len <= 0) {
+        if (wave == 0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[lane * PER + e] = to_storage(0.f, T{});
+            for (int e = 0; e < PER; ++e) o[lane * PER + e] = to_storage(0.f, T{});
+        }
         return;
     }
     const int64_t n64 = (sv.len + p.keys_per_split - 1) / p.keys_per_split;
     const int n = static_cast<int>(min(n64, static_cast<int64_t>(p.n_split)));
     const float *st = p.ws_stats + row * p.n_split * 3;
 
+    // M = max over the splits' m: every thread takes a strided share, then
+    // a wavefront and a workgroup reduction (max is exact in any order).
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, st[3 * s]);
+    for (int s = threadIdx.x; s < n; s += NW * kWave) M = fmaxf(M, st[3 * s]);
+#pragma unroll
+    for (int m = kWave / 2; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+    if (lane == 0) s_max[wave] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_max[w]);
+
+    // Wavefront w sums splits w, w + NW, ... in that order; its loop is
+    // unrolled so that several splits' loads are in flight at once.
     float l = 0.f, c = 0.f, a[PER], bb[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) a[e] = bb[e] = 0.f;
-    for (int s = 0; s < n; ++s) {
+#pragma unroll 4
+    for (int s = wave; s < n; s += NW) {
         const float w = fast_exp2(st[3 * s] - M);
         l += w * st[3 * s + 1];
         c += w * st[3 * s + 2];
@@ -392,6 +411,32 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
         for (int e = 0; e < PER; ++e) {
             a[e] += w * va[e];
             bb[e] += w * vb[e];
+        }
+    }
+    // The wavefronts' partial sums are added in wavefront order.
+    if (lane == 0) {
+        s_red[wave][0] = l;
+        s_red[wave][1] = c;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        s_red[wave][2 + lane * PER + e] = a[e];
+        s_red[wave][2 + D + lane * PER + e] = bb[e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    l = 0.f;
+    c = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) a[e] = bb[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        l += s_red[w][0];
+        c += s_red[w][1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            a[e] += s_red[w][2 + lane * PER + e];
+            bb[e] += s_red[w][2 + D + lane * PER + e];
         }
     }
     const float inv = 1.f / l;
@@ -426,8 +471,8 @@ hipError_t launch_decode_g(const DecodeParams &p, hipStream_t stream) {
     else launch_split<T, D, G, 1>(p, items, stream);
     if (p.n_split > 1) {
         const int64_t rows = static_cast<int64_t>(p.B) * p.Hq;
-        hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(static_cast<uint32_t>(rows)), dim3(kWave), 0,
-                           stream, p);
+        hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(static_cast<uint32_t>(rows)),
+                           dim3(kCombineWaves * kWave), 0, stream, p);
     }
     return hipGetLastError();
 }
