@@ -552,7 +552,7 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(btf / BF16_MFMA_PEAK_TFLOPS, 4),
                              "traffic": btraffic if btraffic is None else round(btraffic),
-                             "kernel": "bwd_rowstat + bwd_dq + bwd_dkdv (one parallax_bwd_prefill call)"},
+                             "kernel": "bwd_dq + bwd_dkdv (one parallax_bwd_prefill call)"},
                 "training_forward_ms": round(fsecs / args.backward_steps * 1e3, 4),
             }
             if not args.no_cpu_baseline:

@@ -159,8 +159,8 @@ size_t parallax_bwd_prefill_workspace_size(int32_t B, int32_t Hq, int32_t T);
  *   workspace    : device, at least parallax_bwd_prefill_workspace_size
  *                  bytes, 16-byte aligned; scratch, contents not kept
  *
- * Three kernels run on `stream`: per-row statistics into the workspace, then
- * dq/drho, then dk/dv.  Every gradient is written in full (no accumulation
+ * Two kernels run on `stream`: dq/drho, which also leaves each row's
+ * statistics in the workspace, then dk/dv.  Every gradient is written in full (no accumulation
  * into the outputs).  Accumulation is fp32; p, w, dS and dR are rounded to
  * bf16 as matrix-core operands.
  *

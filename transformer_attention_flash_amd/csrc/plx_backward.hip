@@ -17,12 +17,13 @@
 // The pages train with this layer but print no backward pass.  With a zero
 // probe these are FlashAttention's gradients (r = rbar = 0, G = D).
 //
-// Three kernels, FlashAttention-2 style, recomputing p from the forward's
+// Two kernels, FlashAttention-2 style, recomputing p from the forward's
 // per-row log2-sum-exp instead of storing it:
-//   bwd_rowstat_kernel  per row: (lse, rbar, G, D)
 //   bwd_dq_kernel       a workgroup of 8 wavefronts owns 128 query rows (as
 //                       the forward) and streams K/V tiles; dq and drho come
-//                       out of one transposed read of the K tile.
+//                       out of one transposed read of the K tile.  It also
+//                       forms each row's (lse, rbar, G, D) and keeps them in
+//                       the workspace for the next kernel.
 //   bwd_dkdv_kernel     a workgroup of 8 wavefronts owns 128 keys (16 per
 //                       wavefront, held in registers) and streams 64-row
 //                       tiles of q, rho and dO over the G query heads of the
@@ -61,52 +62,6 @@ __device__ __forceinline__ void block_order(int id, int n_units, int n_blk, int 
     } else {
         *blk = id / n_units;
         *unit = id % n_units;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Row statistics: rowst[row] = (lse, rbar, G, D).  16 lanes per row.
-// ---------------------------------------------------------------------------
-template <int D, bool HAS_RHO>
-__global__ __launch_bounds__(256) void bwd_rowstat_kernel(BackwardParams p) {
-    constexpr int EPL = D / 16;  // elements per lane
-    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.T;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + threadIdx.x / 16;
-    const int sub = threadIdx.x % 16;
-    float dot_o = 0.f, dot_sa = 0.f;
-    if (row < rows) {
-        const uint16_t *dO = static_cast<const uint16_t *>(p.dout) + row * D + sub * EPL;
-        const uint16_t *o = static_cast<const uint16_t *>(p.out) + row * D + sub * EPL;
-        const uint16_t *osa = HAS_RHO ? static_cast<const uint16_t *>(p.out_sa) + row * D + sub * EPL : nullptr;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-            const u32x2 a = *reinterpret_cast<const u32x2 *>(dO + e);
-            const u32x2 b = *reinterpret_cast<const u32x2 *>(o + e);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                dot_o += bf16_to_f32(a[h] & 0xffffu) * bf16_to_f32(b[h] & 0xffffu);
-                dot_o += bf16_to_f32(a[h] >> 16) * bf16_to_f32(b[h] >> 16);
-            }
-            if constexpr (HAS_RHO) {
-                const u32x2 c = *reinterpret_cast<const u32x2 *>(osa + e);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    dot_sa += bf16_to_f32(a[h] & 0xffffu) * bf16_to_f32(c[h] & 0xffffu);
-                    dot_sa += bf16_to_f32(a[h] >> 16) * bf16_to_f32(c[h] >> 16);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        dot_o += __shfl_xor(dot_o, m);
-        if constexpr (HAS_RHO) dot_sa += __shfl_xor(dot_sa, m);
-    }
-    if (row < rows && sub == 0) {
-        const float rbar = HAS_RHO ? p.rbar[row] : 0.f;
-        const float G = HAS_RHO ? dot_sa : dot_o;
-        const float Dsum = HAS_RHO ? dot_o + rbar * G : dot_o;
-        p.rowst[row] = make_float4(p.lse[row], rbar, G, Dsum);
     }
 }
 
@@ -167,8 +122,40 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
         dop[s] = op8_load(static_cast<const S *>(p.dout) + roff + 32 * s + 8 * grp);
         if constexpr (HAS_RHO) rop[s] = op8_load(static_cast<const S *>(p.rho) + roff + 32 * s + 8 * grp);
     }
-    const float4 st = p.rowst[row];
-    const float lse = st.x, rbar = st.y, Gi = st.z, Di = st.w;
+    // The row's statistics are formed here and kept for the dk/dv kernel:
+    // lse and rbar from the training forward, G = dO . o^SA and
+    // D = dO . o + rbar G.  Each lane holds 32 of the row's head dims (its
+    // four lane groups together hold all of them); two exchanges across the
+    // groups finish the dot products.
+    float dot_o = 0.f, dot_sa = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const Op8<BF16> ov = op8_load(static_cast<const S *>(p.out) + roff + 32 * s + 8 * grp);
+        Op8<BF16> sv;
+        if constexpr (HAS_RHO) sv = op8_load(static_cast<const S *>(p.out_sa) + roff + 32 * s + 8 * grp);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t dw = dop[s].w[h], owd = ov.w[h];
+            dot_o = fmaf(bf16_to_f32(dw & 0xffffu), bf16_to_f32(owd & 0xffffu), dot_o);
+            dot_o = fmaf(bf16_to_f32(dw >> 16), bf16_to_f32(owd >> 16), dot_o);
+            if constexpr (HAS_RHO) {
+                const uint32_t sw = sv.w[h];
+                dot_sa = fmaf(bf16_to_f32(dw & 0xffffu), bf16_to_f32(sw & 0xffffu), dot_sa);
+                dot_sa = fmaf(bf16_to_f32(dw >> 16), bf16_to_f32(sw >> 16), dot_sa);
+            }
+        }
+    }
+    dot_o += __shfl_xor(dot_o, 16);
+    dot_o += __shfl_xor(dot_o, 32);
+    if constexpr (HAS_RHO) {
+        dot_sa += __shfl_xor(dot_sa, 16);
+        dot_sa += __shfl_xor(dot_sa, 32);
+    }
+    const float lse = p.lse[row];
+    const float rbar = HAS_RHO ? p.rbar[row] : 0.f;
+    const float Gi = HAS_RHO ? dot_sa : dot_o;
+    const float Di = HAS_RHO ? dot_o + rbar * Gi : dot_o;
+    if (grp == 0 && pos < T_len) p.rowst[row] = make_float4(lse, rbar, Gi, Di);
 
     int g_off[NKC], l_off[NKC];
 #pragma unroll
@@ -532,15 +519,10 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
 
 template <int D, int G, bool R>
 hipError_t launch_bwd_r(const BackwardParams &p, hipStream_t stream) {
-    const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.T;
-    hipLaunchKernelGGL((bwd_rowstat_kernel<D, R>), dim3(static_cast<uint32_t>((rows + 15) / 16)), dim3(256), 0,
-                       stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t units = static_cast<int64_t>(p.B) * p.Hkv;
     hipLaunchKernelGGL((bwd_dq_kernel<D, G, R>), dim3(static_cast<uint32_t>(units * p.n_qblk)),
                        dim3(kBwdWaves * kWave), 0, stream, p);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, R>), dim3(static_cast<uint32_t>(units * p.n_kblk)),
                        dim3(kBwdWaves * kWave), 0, stream, p);
