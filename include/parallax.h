@@ -222,7 +222,8 @@ size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
  *
  *   q, rho, out : device, [B, Hq, d]; rho may be NULL (softmax only, bitwise
  *                 equal to a zero probe).
- *   k_cache, v_cache : device.
+ *   k_cache, v_cache : device; may be NULL when max_ctx == 0 (every
+ *                 sequence is empty and no key is read).
  *       cu_seqlens == NULL: contiguous cache [B, Hkv, max_ctx, d]; every
  *                 sequence has max_ctx keys.
  *       cu_seqlens != NULL: device int64 [B + 1] token offsets, cu[0] = 0,

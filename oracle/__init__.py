@@ -123,8 +123,11 @@ def attend_rows(q_rows, rho_rows, k_base, v_base, key_off, key_len, key_stride,
     if key_off.size != n or key_len.size != n:
         raise ValueError("key_off/key_len must have one entry per row")
     if n:
-        last = key_off + np.maximum(key_len - 1, 0) * key_stride + d
-        if (key_off < 0).any() or (key_len < 0).any() or int(last.max()) > k_base.size:
+        if (key_off < 0).any() or (key_len < 0).any():
+            raise ValueError("negative key offset or length")
+        used = key_len > 0  # an empty row reads no key
+        last = key_off[used] + (key_len[used] - 1) * key_stride + d
+        if last.size and int(last.max()) > k_base.size:
             raise ValueError("a row's keys fall outside the key storage")
     out = np.zeros((n, d), dtype=np.float64)
     if n == 0:

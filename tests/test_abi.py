@@ -146,6 +146,7 @@ def decode(lib, q=P[0], rho=P[1], k=P[2], v=P[3], cu=None, max_ctx=4096, out=P[4
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
+    (dict(k=None, max_ctx=1), INVALID),        # a cache without storage is only allowed when it is empty
     (dict(B=0), INVALID), (dict(max_ctx=-1), INVALID), (dict(Hq=5, Hkv=2), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(ks=16), INVALID), (dict(ks=48), INVALID), (dict(ks=-32), INVALID), (dict(ks=(1 << 20) + 32), INVALID),

@@ -378,3 +378,20 @@ def test_planted_mistakes_are_caught(oracle_mod, tmp_path, name):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+def test_empty_context_reads_no_key(oracle_mod):
+    """A sequence with no key returns zeros, and its bounds check looks at no
+    storage: a batch of empty ragged sequences needs none at all."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((3, 4, 64))
+    rho = 0.1 * rng.standard_normal((3, 4, 64))
+    none = np.zeros(1)
+    out = oracle.decode(q, rho, none, none, 0.125, cu_seqlens=np.zeros(4, dtype=np.int64), Hkv=2)
+    assert out.shape == q.shape and not out.any()
+    # one non-empty sequence among empty ones still has to fit its storage
+    kv = rng.standard_normal(2 * 5 * 64)
+    out = oracle.decode(q, rho, kv, kv, 0.125, cu_seqlens=np.array([0, 0, 5, 5]), Hkv=2)
+    assert not out[0].any() and not out[2].any() and np.abs(out[1]).max() > 0
+    with pytest.raises(ValueError):
+        oracle.decode(q, rho, kv[:-1], kv[:-1], 0.125, cu_seqlens=np.array([0, 0, 5, 5]), Hkv=2)

@@ -306,7 +306,10 @@ plx_status_t parallax_fwd_decode(const void *q, const void *rho, const void *k_c
                                  int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype,
                                  int32_t keys_per_split, void *workspace, size_t workspace_bytes,
                                  plx_stream_t stream) {
-    if (!q || !k_cache || !v_cache || !out) return PLX_ERR_INVALID_ARGUMENT;
+    if (!q || !out) return PLX_ERR_INVALID_ARGUMENT;
+    // With max_ctx == 0 every sequence is empty and no key is read, so an
+    // empty cache may come without storage.
+    if (max_ctx != 0 && (!k_cache || !v_cache)) return PLX_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned16(workspace) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0)
         return PLX_ERR_INVALID_ARGUMENT;
