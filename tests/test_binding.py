@@ -91,3 +91,26 @@ def test_projection_shape_checks():
         plx.qkvr_projection(t(1, 8, 64), t(5 * 64, 64), 2, 1, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         plx.qkvr_projection(t(1, 8, 64), t(6 * 64, 64), 2, 1, 64)
+
+
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor on a machine without one: only the
+    attributes the binding's checks read."""
+
+    def __init__(self, index, dtype=BF):
+        self.is_cuda = True
+        self.dtype = dtype
+        self.device = torch.device("cuda", index)
+
+    def is_contiguous(self):
+        return True
+
+
+def test_tensors_on_two_devices_are_rejected():
+    from transformer_attention_flash_amd import api
+    a, b = _FakeGpuTensor(0), _FakeGpuTensor(1)
+    with pytest.raises(ValueError, match="other tensors are on cuda:0"):
+        api._check_tensors(BF, q=a, k=b)
+    with pytest.raises(ValueError, match="workspace is on cuda:1"):
+        api._check_device(q=a, workspace=b)
+    api._check_device(q=a, k=_FakeGpuTensor(0), rho=None)  # one device: accepted

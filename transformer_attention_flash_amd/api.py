@@ -24,7 +24,28 @@ def _ptr(t: Optional[torch.Tensor]):
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
+    dev = getattr(stream, "device", None)
+    if dev is not None and dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"stream belongs to {dev} but the current device is cuda:{torch.cuda.current_device()}")
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_device(**tensors):
+    """All given GPU tensors on one device, and that device the current one:
+    the kernels launch on the current device's stream, which must be able to
+    address every pointer."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors are on {dev}")
+    if dev is not None and dev.index is not None and torch.cuda.is_available() \
+            and dev.index != torch.cuda.current_device():
+        raise ValueError(f"the tensors are on {dev} but the current device is cuda:{torch.cuda.current_device()}; "
+                         f"call under torch.cuda.device({dev.index})")
 
 
 def _check_tensors(dtype, **tensors):
@@ -37,6 +58,7 @@ def _check_tensors(dtype, **tensors):
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != dtype:
             raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    _check_device(**tensors)
 
 
 def _dtype_code(dtype) -> int:
@@ -130,6 +152,7 @@ def prefill_backward(q, k, v, rho, out, out_sa, lse, rbar, dout, *, scale: Optio
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     elif not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
+    _check_device(q=q, lse=lse, workspace=workspace)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -244,6 +267,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: O
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
+    _check_device(q=q, cu_seqlens=cu_seqlens, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = N.load().parallax_fwd_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
                                       int(max_ctx), _ptr(out), B, Hq, Hkv, d, scale, code, int(keys_per_split),
