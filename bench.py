@@ -9,7 +9,9 @@ causal prefill (B=8, T=4096, Hq=16, Hkv=8, d=128, bf16), is timed the same way
 and reported under "prefill" with its MFMA roofline; the prefill backward
 (parallax_bwd_prefill on the same tensors) under "prefill"/"backward", and the
 fused q/k/v/probe projection of the same layer under "prefill"/"projection"
-(with torch's library GEMM time for the same product as context).
+(with torch's library GEMM time for the same product as context).  As context
+only, "prefill"/"longer_sequence" times the same heads and token count at a
+4x longer sequence (B=2, T=16384).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Several input sets are rotated so that no step finds its K/V in the 256 MB
@@ -484,6 +486,20 @@ def main():
             "softmax_only": {"value": round(stf, 2), "unit": "TFLOP/s",
                              "ms_per_step": round(ssecs / args.prefill_steps * 1e3, 4)},
         }
+        # Context only: the same heads and token count (B * T = 32768) at a longer sequence, where
+        # a workgroup's fixed start-up cost is spread over 4x as many key tiles.
+        lb, lt = max(1, pw.B // 4), pw.T * 4
+        lx = synth.make_prefill(lb, pw.Hq, pw.Hkv, lt, pw.d, pw.dtype, dev, seed=7)
+        lout = torch.empty_like(lx["q"])
+        lsecs, _ = time_steps(lambda i: plx.prefill(lx["q"], lx["k"], lx["v"], lx["rho"], out=lout),
+                              max(2, args.prefill_steps // 5), max(2, args.prefill_warmup // 5), torch)
+        lsteps = max(2, args.prefill_steps // 5)
+        ltf = 4 * 2 * pw.d * lb * pw.Hq * lt * (lt + 1) // 2 / (lsecs / lsteps) / 1e12
+        log(f"prefill B={lb} T={lt}: {lsecs / lsteps * 1e3:.3f} ms/step, {ltf:.1f} TFLOP/s")
+        result["prefill"]["longer_sequence"] = {
+            "B": lb, "T": lt, "value": round(ltf, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(lsecs / lsteps * 1e3, 4), "frac_of_peak": round(ltf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del lx, lout
         if not args.no_cpu_baseline:
             log("prefill CPU baseline (oracle)")
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
