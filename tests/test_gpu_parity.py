@@ -247,3 +247,27 @@ def test_stream_argument_is_honoured():
     b = plx.decode(x["q"], x["k"], x["v"], x["rho"])
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state between calls: decodes (each with its own
+    workspace, several chunks so the merge kernel runs) and prefills issued
+    on two streams at once give the same bits as the same calls run one
+    after another."""
+    say("two streams at once")
+    xd = [synth.make_decode(3, 8, 4, 1500, 128, BF, DEV, seed=20 + i) for i in range(2)]
+    xp = [synth.make_prefill(1, 4, 2, 300, 128, BF, DEV, seed=30 + i) for i in range(2)]
+    ref_d = [plx.decode(x["q"], x["k"], x["v"], x["rho"], keys_per_split=256) for x in xd]
+    ref_p = [plx.prefill(x["q"], x["k"], x["v"], x["rho"]) for x in xp]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got_d, got_p = [None, None], [None, None]
+    for rep in range(3):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                got_d[i] = plx.decode(xd[i]["q"], xd[i]["k"], xd[i]["v"], xd[i]["rho"], keys_per_split=256)
+                got_p[i] = plx.prefill(xp[i]["q"], xp[i]["k"], xp[i]["v"], xp[i]["rho"])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(got_d[i], ref_d[i]), f"decode on stream {i}, repetition {rep}"
+            assert torch.equal(got_p[i], ref_p[i]), f"prefill on stream {i}, repetition {rep}"
