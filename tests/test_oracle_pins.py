@@ -284,10 +284,12 @@ def _brute_row(q, rho, keys, vals, tau):
     return out
 
 
-def pin_bruteforce_layouts(lib):
+def pin_bruteforce_layouts(lib, mod=oracle):
     """Pure-Python loops over nested per-sequence lists check the index
     mapping: causal keys 0..t with the diagonal, query head h on KV head
-    h // G, packed ragged slabs (including an empty sequence: output 0)."""
+    h // G, packed ragged slabs (including an empty sequence: output 0), and
+    the contiguous cache [B, Hkv, L, d].  `mod` is the oracle module (the
+    planted-mistake test passes broken copies of it)."""
     rng = np.random.default_rng(21)
     B, Hq, Hkv, T, d, tau = 2, 4, 2, 5, 3, 0.8
     G = Hq // Hkv
@@ -296,7 +298,7 @@ def pin_bruteforce_layouts(lib):
     k = rng.standard_normal((B, Hkv, T, d))
     v = rng.standard_normal((B, Hkv, T, d))
     for form in FORMS:
-        got = oracle.prefill(q, k, v, rho, tau, form=form, lib=lib)
+        got = mod.prefill(q, k, v, rho, tau, form=form, lib=lib)
         for b in range(B):
             for h in range(Hq):
                 for t in range(T):
@@ -314,14 +316,25 @@ def pin_bruteforce_layouts(lib):
     qd = rng.standard_normal((len(lens), Hq, d))
     rd = rng.standard_normal((len(lens), Hq, d))
     for form in FORMS:
-        got = oracle.decode(qd, rd, packed_k, packed_v, tau, cu_seqlens=cu, Hkv=Hkv,
-                            form=form, lib=lib)
+        got = mod.decode(qd, rd, packed_k, packed_v, tau, cu_seqlens=cu, Hkv=Hkv,
+                         form=form, lib=lib)
         for b, n in enumerate(lens):
             for h in range(Hq):
                 keys = [list(seqs_k[b][h // G, j]) for j in range(n)]
                 vals = [list(seqs_v[b][h // G, j]) for j in range(n)]
                 want = _brute_row(list(qd[b, h]), list(rd[b, h]), keys, vals, tau)
                 assert np.allclose(got[b, h], want, rtol=0, atol=1e-12), (b, h, form)
+    # contiguous decode cache: every sequence has all L keys of its own [Hkv, L, d] block
+    L = 4
+    kc = rng.standard_normal((len(lens), Hkv, L, d))
+    vc = rng.standard_normal((len(lens), Hkv, L, d))
+    for form in FORMS:
+        got = mod.decode(qd, rd, kc, vc, tau, form=form, lib=lib)
+        for b in range(len(lens)):
+            for h in range(Hq):
+                want = _brute_row(list(qd[b, h]), list(rd[b, h]), [list(x) for x in kc[b, h // G]],
+                                  [list(x) for x in vc[b, h // G]], tau)
+                assert np.allclose(got[b, h], want, rtol=0, atol=1e-12), (b, h, form, "contiguous")
 
 
 PINS = [pin_hand_example, pin_rho_zero_is_softmax_attention, pin_one_key,
@@ -395,3 +408,30 @@ def test_empty_context_reads_no_key(oracle_mod):
     assert not out[0].any() and not out[2].any() and np.abs(out[1]).max() > 0
     with pytest.raises(ValueError):
         oracle.decode(q, rho, kv[:-1], kv[:-1], 0.125, cu_seqlens=np.array([0, 0, 5, 5]), Hkv=2)
+
+
+# Planted mistakes in the Python half of the oracle (the index mapping onto
+# rows): each must make the brute-force layout pin fail.
+PY_MUTATIONS = {
+    "prefill_gqa_interleaved": ("key_off = ((b * Hkv + h // G) * T) * d", "key_off = ((b * Hkv + h % Hkv) * T) * d"),
+    "prefill_diagonal_dropped": ("key_len = t + 1", "key_len = np.maximum(t, 1)"),
+    "decode_gqa_interleaved": ("key_off = (starts[b] * Hkv + (h // G) * lens[b]) * d",
+                               "key_off = (starts[b] * Hkv + (h % Hkv) * lens[b]) * d"),
+    "decode_slab_start_per_token": ("key_off = (starts[b] * Hkv + (h // G) * lens[b]) * d",
+                                    "key_off = (starts[b] + (h // G) * lens[b]) * d"),
+    "decode_contiguous_stride": ("starts = np.arange(B, dtype=np.int64) * L", "starts = np.arange(B, dtype=np.int64) * (L - 1)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTATIONS))
+def test_planted_python_mapping_mistakes_are_caught(oracle_mod, name):
+    import types
+    path = oracle.__file__
+    src = open(path).read()
+    old, new = PY_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor not unique: {old}"
+    mutant = types.ModuleType("oracle_mutant")
+    mutant.__file__ = path  # the mutant loads the real C library next to it
+    exec(compile(src.replace(old, new), path, "exec"), mutant.__dict__)
+    with pytest.raises((AssertionError, ValueError)):
+        pin_bruteforce_layouts(None, mod=mutant)
