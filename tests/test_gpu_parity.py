@@ -47,6 +47,8 @@ DECODE_CASES = [
     (2, 4, 2, 300, 128, F32, 64),
     (2, 4, 4, 64, 64, F32, 0),
     (1, 8, 1, 45, 128, F32, 32),     # G = 8, fp32
+    (2, 4, 2, 4096, 128, BF, 32),    # 128 chunks per sequence: the merge's wavefronts each sum 32
+    (1, 4, 2, 32768, 64, BF, 32),    # 1024 chunks per sequence
 ]
 
 
