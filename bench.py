@@ -10,8 +10,10 @@ and reported under "prefill" with its MFMA roofline; the prefill backward
 (parallax_bwd_prefill on the same tensors) under "prefill"/"backward", and the
 fused q/k/v/probe projection of the same layer under "prefill"/"projection"
 (with torch's library GEMM time for the same product as context).  As context
-only, "prefill"/"longer_sequence" times the same heads and token count at a
-4x longer sequence (B=2, T=16384).
+only (skipped with --no-context), "prefill"/"longer_sequence" times the same heads and token count at a
+4x longer sequence (B=2, T=16384), and "decode_other_workloads" the two decode
+extremes (2048 x 128 keys, 256 x 32768 keys) and the ragged batch (2048
+sequences of 128..32768 keys, Hq=32, Hkv=16, d=64).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Several input sets are rotated so that no step finds its K/V in the 256 MB
@@ -333,6 +335,43 @@ def run_sweep(args, torch, plx, synth):
         print(json.dumps(row), flush=True)
 
 
+def other_decode_workloads(plx, synth, dev, torch):
+    """The two decode extremes and the ragged batch, timed like the headline
+    (one call over the whole batch is one step), as context: GB/s of K/V and
+    its fraction of the HBM peak.  Small caches rotate 4 input sets; the
+    large ones (34 GB, 138 GB of K/V) are far beyond the Infinity Cache with
+    one."""
+    res = {}
+    for name, n_sets, steps, warmup in (("decode_bf16_b2048_hq16_hkv8_l128_d128", 4, 50, 20),
+                                        ("decode_bf16_b256_hq16_hkv8_l32768_d128", 1, 10, 3),
+                                        ("decode_ragged_bf16_b2048_hq32_hkv16_d64_l128to32768", 1, 5, 2)):
+        w = synth.WORKLOADS[name]
+        log(f"decode workload {name}")
+        if w.kind == "decode_ragged":
+            xs = [synth.make_workload(w, dev)]
+            kv = 2 * 2 * w.Hkv * w.d * int(xs[0]["cu_host"][-1])
+            kw = dict(cu_seqlens=xs[0]["cu_seqlens"], max_ctx=xs[0]["max_ctx"], num_kv_heads=w.Hkv)
+        else:
+            xs = [synth.make_decode(w.B, w.Hq, w.Hkv, w.L, w.d, w.dtype, dev, seed=s) for s in range(n_sets)]
+            kv = 2 * 2 * w.B * w.Hkv * w.L * w.d
+            kw = {}
+        out = torch.empty_like(xs[0]["q"])
+
+        def step(i, xs=xs, kw=kw, out=out):
+            x = xs[i % len(xs)]
+            plx.decode(x["q"], x["k"], x["v"], x["rho"], out=out, **kw)
+
+        secs, _ = time_steps(step, steps, warmup, torch)
+        gbs = kv / (secs / steps) / 1e9
+        res[name] = {"value": round(gbs, 2), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "ms_per_step": round(secs / steps * 1e3, 4), "steps": steps, "kv_bytes": kv,
+                     "input_sets_rotated": len(xs)}
+        log(f"  {secs / steps * 1e3:.3f} ms/step, {gbs:.0f} GB/s")
+        del xs, out, kw
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +387,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-projection", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context-only legs (longer-sequence prefill, other decode workloads)")
     ap.add_argument("--no-device", action="store_true", help="skip the device ceiling measurements")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--backward-warmup", type=int, default=20)
@@ -445,6 +486,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline_decode(sets[0], w, args.cpu_budget)
     del sets
     torch.cuda.empty_cache()
+    if not args.no_context:
+        result["decode_other_workloads"] = other_decode_workloads(plx, synth, dev, torch)
 
     # ---------------- prefill ----------------
     if not args.no_prefill:
@@ -486,20 +529,21 @@ def main():
             "softmax_only": {"value": round(stf, 2), "unit": "TFLOP/s",
                              "ms_per_step": round(ssecs / args.prefill_steps * 1e3, 4)},
         }
-        # Context only: the same heads and token count (B * T = 32768) at a longer sequence, where
-        # a workgroup's fixed start-up cost is spread over 4x as many key tiles.
-        lb, lt = max(1, pw.B // 4), pw.T * 4
-        lx = synth.make_prefill(lb, pw.Hq, pw.Hkv, lt, pw.d, pw.dtype, dev, seed=7)
-        lout = torch.empty_like(lx["q"])
-        lsecs, _ = time_steps(lambda i: plx.prefill(lx["q"], lx["k"], lx["v"], lx["rho"], out=lout),
-                              max(2, args.prefill_steps // 5), max(2, args.prefill_warmup // 5), torch)
-        lsteps = max(2, args.prefill_steps // 5)
-        ltf = 4 * 2 * pw.d * lb * pw.Hq * lt * (lt + 1) // 2 / (lsecs / lsteps) / 1e12
-        log(f"prefill B={lb} T={lt}: {lsecs / lsteps * 1e3:.3f} ms/step, {ltf:.1f} TFLOP/s")
-        result["prefill"]["longer_sequence"] = {
-            "B": lb, "T": lt, "value": round(ltf, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(lsecs / lsteps * 1e3, 4), "frac_of_peak": round(ltf / BF16_MFMA_PEAK_TFLOPS, 4)}
-        del lx, lout
+        if not args.no_context:
+            # Context only: the same heads and token count (B * T = 32768) at a longer sequence, where
+            # a workgroup's fixed start-up cost is spread over 4x as many key tiles.
+            lb, lt = max(1, pw.B // 4), pw.T * 4
+            lx = synth.make_prefill(lb, pw.Hq, pw.Hkv, lt, pw.d, pw.dtype, dev, seed=7)
+            lout = torch.empty_like(lx["q"])
+            lsecs, _ = time_steps(lambda i: plx.prefill(lx["q"], lx["k"], lx["v"], lx["rho"], out=lout),
+                                  max(2, args.prefill_steps // 5), max(2, args.prefill_warmup // 5), torch)
+            lsteps = max(2, args.prefill_steps // 5)
+            ltf = 4 * 2 * pw.d * lb * pw.Hq * lt * (lt + 1) // 2 / (lsecs / lsteps) / 1e12
+            log(f"prefill B={lb} T={lt}: {lsecs / lsteps * 1e3:.3f} ms/step, {ltf:.1f} TFLOP/s")
+            result["prefill"]["longer_sequence"] = {
+                "B": lb, "T": lt, "value": round(ltf, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(lsecs / lsteps * 1e3, 4), "frac_of_peak": round(ltf / BF16_MFMA_PEAK_TFLOPS, 4)}
+            del lx, lout
         if not args.no_cpu_baseline:
             log("prefill CPU baseline (oracle)")
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
