@@ -40,3 +40,25 @@ def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_profile_commands_run_with_the_flags_bench_accepts():
+    """Every bench.py command recorded in profiles/ uses only flags the
+    benchmark accepts, and leaves out the context-only legs (--no-context), so
+    that it reproduces the dispatch sequence its summary describes."""
+    import re
+    import subprocess
+    helptext = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True,
+                              text=True, timeout=120).stdout
+    prof = os.path.join(ROOT, "profiles")
+    n = 0
+    for name in sorted(os.listdir(prof)):
+        for line in open(os.path.join(prof, name)):
+            if "python3 bench.py" not in line:
+                continue
+            n += 1
+            args = line.split("python3 bench.py", 1)[1].split()
+            for flag in (a for a in args if a.startswith("--")):
+                assert re.search(rf"(^|\s){re.escape(flag)}(\s|$|,)", helptext), f"{name}: unknown flag {flag}"
+            assert "--no-context" in args, f"{name}: command runs the context legs"
+    assert n >= 6
