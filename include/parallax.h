@@ -37,7 +37,7 @@
  *
  * Memory.  Every pointer argument named as "device" is device memory owned by
  * the caller; the library never allocates, frees or synchronises.  Calls are
- * asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
+ * asynchronous on `stream` (NULL is the null stream) and
  * return as soon as the kernels are queued.  A device fault surfaces at the
  * caller's next synchronisation.  All tensors are dense, row-major, with the
  * head dimension innermost, and start on a 16-byte boundary (cu_seqlens: 8
@@ -56,6 +56,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -73,12 +75,12 @@ typedef enum {
     PLX_DTYPE_BF16 = 1   /* bfloat16 inputs and output (round to nearest even) */
 } plx_dtype_t;
 
-/* A hipStream_t, passed as an opaque pointer so this header needs no HIP
- * include.  NULL selects the null stream. */
-typedef void *plx_stream_t;
-
 /*
- * Causal prefill (T query tokens over the same T keys).
+ * Causal prefill (T query tokens over the same T keys): the forward pass of
+ * the layer over a whole sequence, as in language-model pretraining (the
+ * news.chathome.org article, "Experiments"), with the probe rho = W_R x given
+ * as an input (same article, "What is Parallax"; gist.science summary,
+ * "Method: Parallax / core mechanism").
  *
  *   q, rho, out : device, [B, Hq, T, d]
  *   k, v        : device, [B, Hkv, T, d]
@@ -97,7 +99,7 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v,
                                   const void *rho, void *out,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
                                   int32_t d, float softmax_scale,
-                                  plx_dtype_t dtype, plx_stream_t stream);
+                                  plx_dtype_t dtype, hipStream_t stream);
 
 /*
  * Causal prefill forward that also keeps what parallax_bwd_prefill needs
@@ -125,7 +127,7 @@ plx_status_t parallax_fwd_prefill_train(const void *q, const void *k,
                                         float *rbar, int32_t B, int32_t Hq,
                                         int32_t Hkv, int32_t T, int32_t d,
                                         float softmax_scale, plx_dtype_t dtype,
-                                        plx_stream_t stream);
+                                        hipStream_t stream);
 
 /*
  * Bytes of device workspace parallax_bwd_prefill needs: 16 bytes per query
@@ -178,7 +180,7 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
                                   int32_t d, float softmax_scale,
                                   plx_dtype_t dtype, void *workspace,
-                                  size_t workspace_bytes, plx_stream_t stream);
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fused q/k/v/probe projection: the probe is a learned linear map of the
@@ -203,22 +205,16 @@ plx_status_t parallax_qkvr_projection(const void *x, const void *w, void *q,
                                       void *k, void *v, void *rho, int32_t B,
                                       int32_t T, int32_t d_model, int32_t Hq,
                                       int32_t Hkv, int32_t d,
-                                      plx_dtype_t dtype, plx_stream_t stream);
+                                      plx_dtype_t dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace parallax_fwd_decode needs for these sizes and
- * this split setting (keys_per_split as passed to parallax_fwd_decode; 0 =
- * the library's own choice).  Returns 0 when the call needs no workspace
- * (a single split), and (size_t)-1 for arguments parallax_fwd_decode would
- * reject.
- */
-size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
-                                          int32_t d, int64_t max_ctx,
-                                          plx_dtype_t dtype,
-                                          int32_t keys_per_split);
-
-/*
- * Decode: one query token per sequence over a KV cache.
+ * Decode: one query token per sequence over a KV cache.  Parallax keeps the
+ * softmax form, so decoding reads a KV cache as softmax attention does (the
+ * zubnet.ai news item on Parallax, mechanism paragraph), and each decode step
+ * supplies a single query row per head (the news.chathome.org article,
+ * "Hardware argument").  The library chooses how each sequence is cut into
+ * chunks (one workgroup each, merged by a second kernel when there are
+ * several); parallax_fwd_decode_chunked takes that choice from the caller.
  *
  *   q, rho, out : device, [B, Hq, d]; rho may be NULL (softmax only, bitwise
  *                 equal to a zero probe).
@@ -234,32 +230,76 @@ size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
  *                 well-formed cu_seqlens (it lives on the device and is not
  *                 checked).
  *   max_ctx     : >= 0; the longest context.
- *   keys_per_split: 0 lets the library choose; otherwise a multiple of 32 in
- *                 [32, 2^20].  A sequence is cut into chunks of that many keys,
- *                 one workgroup each, and the chunks are merged by a second
- *                 kernel.  Any setting gives the same result up to fp32
- *                 rounding.
+ *   softmax_scale: tau > 0 and finite (usually 1/sqrt(d)).
  *   workspace   : device, at least parallax_fwd_decode_workspace_size(...)
  *                 bytes (may be NULL when that size is 0); holds the
  *                 per-chunk partial results; contents are scratch.
  *
  * Supported: d in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; dtype BF16 (F32 is
- * accepted as a debugging aid).  Errors as for prefill, plus
- * PLX_ERR_WORKSPACE_TOO_SMALL.
+ * accepted as a debugging aid).  Returns PLX_ERR_INVALID_ARGUMENT for null
+ * q/out (or null k/v with max_ctx > 0), misaligned pointers, non-positive
+ * sizes, Hq not a multiple of Hkv, a bad scale or an output overlapping an
+ * input or the workspace; PLX_ERR_UNSUPPORTED for other d, group sizes or
+ * dtypes, or more than 2^31 - 1 workgroups; PLX_ERR_WORKSPACE_TOO_SMALL.
  */
 plx_status_t parallax_fwd_decode(const void *q, const void *rho,
                                  const void *k_cache, const void *v_cache,
                                  const int64_t *cu_seqlens, int64_t max_ctx,
                                  void *out, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t d, float softmax_scale,
-                                 plx_dtype_t dtype, int32_t keys_per_split,
-                                 void *workspace, size_t workspace_bytes,
-                                 plx_stream_t stream);
+                                 plx_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
-/* Keys per chunk that parallax_fwd_decode uses for keys_per_split == 0, or a
+/*
+ * Bytes of device workspace parallax_fwd_decode needs for these sizes: 0 when
+ * the library runs one chunk per sequence (no merge), and (size_t)-1 for
+ * arguments parallax_fwd_decode would reject.
+ */
+size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
+                                          int32_t d, int64_t max_ctx,
+                                          plx_dtype_t dtype);
+
+/* Keys per chunk that parallax_fwd_decode uses for these sizes, or a
  * negative plx_status_t value for rejected arguments. */
 int32_t parallax_fwd_decode_auto_split(int32_t B, int32_t Hq, int32_t Hkv,
                                        int32_t d, int64_t max_ctx);
+
+/*
+ * parallax_fwd_decode with the chunking chosen by the caller: each sequence
+ * is cut into chunks of keys_per_split keys, one workgroup each, and the
+ * chunks are merged by a second kernel (the associative merge of the
+ * per-chunk softmax states).  Any setting gives the same result up to fp32
+ * rounding.  For tests, sweeps and tuning; parallax_fwd_decode picks the
+ * setting itself.
+ *
+ *   keys_per_split: 0 = the library's choice (then the call is exactly
+ *                 parallax_fwd_decode); otherwise a multiple of 32 in
+ *                 [32, 2^20].
+ *   workspace   : at least parallax_fwd_decode_chunked_workspace_size(...,
+ *                 keys_per_split) bytes.
+ *
+ * Other arguments, errors and conventions as parallax_fwd_decode; a
+ * keys_per_split outside the range returns PLX_ERR_INVALID_ARGUMENT.
+ */
+plx_status_t parallax_fwd_decode_chunked(const void *q, const void *rho,
+                                         const void *k_cache,
+                                         const void *v_cache,
+                                         const int64_t *cu_seqlens,
+                                         int64_t max_ctx, void *out, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d,
+                                         float softmax_scale, plx_dtype_t dtype,
+                                         int32_t keys_per_split,
+                                         void *workspace,
+                                         size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Workspace bytes of parallax_fwd_decode_chunked for this keys_per_split
+ * (0 = the library's choice), or (size_t)-1 for rejected arguments. */
+size_t parallax_fwd_decode_chunked_workspace_size(int32_t B, int32_t Hq,
+                                                  int32_t Hkv, int32_t d,
+                                                  int64_t max_ctx,
+                                                  plx_dtype_t dtype,
+                                                  int32_t keys_per_split);
 
 /* A static, human-readable name for a status code. */
 const char *parallax_status_string(plx_status_t s);

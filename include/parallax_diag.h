@@ -54,7 +54,7 @@ plx_status_t parallax_diag_device_info(int32_t device, int32_t *cu_count,
  */
 plx_status_t parallax_diag_stream_read(const void *src, size_t bytes,
                                        int32_t nontemporal, void *sink,
-                                       plx_stream_t stream);
+                                       hipStream_t stream);
 
 /*
  * Matrix-core throughput: n_blocks workgroups of 4 wavefronts, each wavefront
@@ -70,7 +70,7 @@ plx_status_t parallax_diag_stream_read(const void *src, size_t bytes,
  * [1, 2^20] or iterations outside [1, 2^24].
  */
 plx_status_t parallax_diag_mfma_bf16(void *sink, int32_t n_blocks,
-                                     int32_t iterations, plx_stream_t stream);
+                                     int32_t iterations, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -110,14 +110,14 @@ int main(int argc, char **argv) {
     if (is_prefill) {
         st = parallax_fwd_prefill(q, k, v, rho, out, B, Hq, Hkv, (int32_t)N, d, scale, PLX_DTYPE_BF16, stream);
     } else {
-        const size_t ws_bytes = parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, N, PLX_DTYPE_BF16, 0);
+        const size_t ws_bytes = parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, N, PLX_DTYPE_BF16);
         if (ws_bytes == (size_t)-1) return fail("status", "workspace size query rejected the shape");
         if (ws_bytes && hipMalloc(&ws, ws_bytes) != hipSuccess) return fail("hip", "workspace");
         if (ws_bytes && parallax_fwd_decode(q, rho, k, v, cu_dev, N, out, B, Hq, Hkv, d, scale,
-                                            PLX_DTYPE_BF16, 0, ws, ws_bytes - 1, stream) !=
+                                            PLX_DTYPE_BF16, ws, ws_bytes - 1, stream) !=
                             PLX_ERR_WORKSPACE_TOO_SMALL)
             return fail("status", "short workspace must be PLX_ERR_WORKSPACE_TOO_SMALL");
-        st = parallax_fwd_decode(q, rho, k, v, cu_dev, N, out, B, Hq, Hkv, d, scale, PLX_DTYPE_BF16, 0, ws,
+        st = parallax_fwd_decode(q, rho, k, v, cu_dev, N, out, B, Hq, Hkv, d, scale, PLX_DTYPE_BF16, ws,
                                  ws_bytes, stream);
     }
     if (st != PLX_OK) return fail("call", parallax_status_string(st));

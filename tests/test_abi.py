@@ -139,41 +139,59 @@ def test_backward_workspace_size(lib):
 
 
 def decode(lib, q=P[0], rho=P[1], k=P[2], v=P[3], cu=None, max_ctx=4096, out=P[4], B=2, Hq=4, Hkv=2, d=128,
-           scale=0.088, dtype=BF16, ks=0, ws=P[5], ws_bytes=1 << 30):
-    return lib.parallax_fwd_decode(q, rho, k, v, cu, max_ctx, out, B, Hq, Hkv, d, scale, dtype, ks, ws, ws_bytes,
-                                   None)
+           scale=0.088, dtype=BF16, ks=None, ws=P[5], ws_bytes=1 << 30):
+    """parallax_fwd_decode, or parallax_fwd_decode_chunked when ks is given."""
+    if ks is None:
+        return lib.parallax_fwd_decode(q, rho, k, v, cu, max_ctx, out, B, Hq, Hkv, d, scale, dtype, ws, ws_bytes,
+                                       None)
+    return lib.parallax_fwd_decode_chunked(q, rho, k, v, cu, max_ctx, out, B, Hq, Hkv, d, scale, dtype, ks, ws,
+                                           ws_bytes, None)
 
 
-@pytest.mark.parametrize("kw,code", [
+DECODE_REJECTIONS = [
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
     (dict(k=None, max_ctx=1), INVALID),        # a cache without storage is only allowed when it is empty
     (dict(B=0), INVALID), (dict(max_ctx=-1), INVALID), (dict(Hq=5, Hkv=2), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
-    (dict(ks=16), INVALID), (dict(ks=48), INVALID), (dict(ks=-32), INVALID), (dict(ks=(1 << 20) + 32), INVALID),
     (dict(d=32), UNSUP), (dict(Hq=48, Hkv=2), UNSUP), (dict(dtype=3), UNSUP),
-    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),  # B=2 x 2 KV heads x 4096 keys: the library splits
     (dict(out=P[0] + 16), INVALID),            # out overlaps q
     (dict(out=P[5]), INVALID),                 # out overlaps the workspace
     (dict(k=P[2] + 2), INVALID), (dict(ws=P[5] + 8), INVALID), (dict(cu=P[6] + 4), INVALID),  # alignment
-])
+]
+
+
+@pytest.mark.parametrize("kw,code", DECODE_REJECTIONS)
 def test_decode_rejections(lib, kw, code):
     assert decode(lib, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", DECODE_REJECTIONS + [
+    (dict(ks=16), INVALID), (dict(ks=48), INVALID), (dict(ks=-32), INVALID), (dict(ks=(1 << 20) + 32), INVALID),
+])
+def test_decode_chunked_rejections(lib, kw, code):
+    assert decode(lib, **{"ks": 256, **kw}) == code
+
+
 def test_decode_workspace_size(lib):
     f = lib.parallax_fwd_decode_workspace_size
+    fc = lib.parallax_fwd_decode_chunked_workspace_size
     # single chunk: no workspace
-    assert f(2048, 16, 8, 128, 128, BF16, 0) == 0
-    assert f(4, 16, 8, 128, 100, BF16, 128) == 0
+    assert f(2048, 16, 8, 128, 128, BF16) == 0
+    assert fc(4, 16, 8, 128, 100, BF16, 128) == 0
     # explicit chunks: stats (3 floats, padded to 256 B) + A and B vectors
     B, Hq, d, L, ks = 3, 8, 64, 1000, 64
     n = -(-L // ks)
     slots = B * Hq * n
     stats = (slots * 3 * 4 + 255) // 256 * 256
-    assert f(B, Hq, 4, d, L, BF16, ks) == stats + slots * 2 * d * 4
-    assert f(B, Hq, 3, d, L, BF16, ks) == SIZE_MAX     # Hq % Hkv
-    assert f(B, Hq, 4, 80, L, BF16, ks) == SIZE_MAX    # head dim
-    assert f(B, Hq, 4, d, L, BF16, 40) == SIZE_MAX     # not a multiple of 32
+    assert fc(B, Hq, 4, d, L, BF16, ks) == stats + slots * 2 * d * 4
+    assert fc(B, Hq, 3, d, L, BF16, ks) == SIZE_MAX     # Hq % Hkv
+    assert fc(B, Hq, 4, 80, L, BF16, ks) == SIZE_MAX    # head dim
+    assert fc(B, Hq, 4, d, L, BF16, 40) == SIZE_MAX     # not a multiple of 32
+    # the library's own choice: the chunked query with 0, and the chunk size it reports
+    for shape in [(1, 16, 8, 128, 4096), (2, 4, 2, 128, 4096), (64, 16, 8, 128, 4096), (3, 8, 4, 64, 1000)]:
+        assert f(*shape, BF16) == fc(*shape, BF16, 0) == fc(*shape, BF16, lib.parallax_fwd_decode_auto_split(*shape))
+    assert f(3, 8, 3, 64, 1000, BF16) == SIZE_MAX
 
 
 def test_decode_auto_split(lib):

@@ -26,9 +26,11 @@ EXPORTS = (
     "parallax_bwd_prefill_workspace_size",
     "parallax_bwd_prefill",
     "parallax_qkvr_projection",
-    "parallax_fwd_decode_workspace_size",
     "parallax_fwd_decode",
+    "parallax_fwd_decode_workspace_size",
     "parallax_fwd_decode_auto_split",
+    "parallax_fwd_decode_chunked",
+    "parallax_fwd_decode_chunked_workspace_size",
     "parallax_status_string",
     "parallax_diag_device_info",
     "parallax_diag_stream_read",
@@ -69,11 +71,16 @@ def load():
     lib.parallax_bwd_prefill.restype = ctypes.c_int
     lib.parallax_qkvr_projection.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_int, vp]
     lib.parallax_qkvr_projection.restype = ctypes.c_int
-    lib.parallax_fwd_decode_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int, i32]
+    lib.parallax_fwd_decode_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int]
     lib.parallax_fwd_decode_workspace_size.restype = ctypes.c_size_t
     lib.parallax_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32, ctypes.c_int,
-                                        i32, vp, ctypes.c_size_t, vp]
+                                        vp, ctypes.c_size_t, vp]
     lib.parallax_fwd_decode.restype = ctypes.c_int
+    lib.parallax_fwd_decode_chunked_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.c_int, i32]
+    lib.parallax_fwd_decode_chunked_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_fwd_decode_chunked.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32,
+                                                ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
+    lib.parallax_fwd_decode_chunked.restype = ctypes.c_int
     lib.parallax_fwd_decode_auto_split.argtypes = [i32, i32, i32, i32, i64]
     lib.parallax_fwd_decode_auto_split.restype = i32
     lib.parallax_status_string.argtypes = [ctypes.c_int]

@@ -208,8 +208,14 @@ def qkvr_projection(x: torch.Tensor, w: torch.Tensor, Hq: int, Hkv: int, d: int,
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype=torch.bfloat16,
                           keys_per_split: int = 0) -> int:
-    n = N.load().parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype),
-                                                     int(keys_per_split))
+    """Workspace bytes of a decode call: parallax_fwd_decode_workspace_size, or
+    with keys_per_split != 0 parallax_fwd_decode_chunked_workspace_size."""
+    lib = N.load()
+    if keys_per_split:
+        n = lib.parallax_fwd_decode_chunked_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype),
+                                                           int(keys_per_split))
+    else:
+        n = lib.parallax_fwd_decode_workspace_size(B, Hq, Hkv, d, int(max_ctx), _dtype_code(dtype))
     if n == (1 << 64) - 1:
         raise N.ParallaxError(N.PLX_ERR_INVALID_ARGUMENT, "parallax_fwd_decode_workspace_size")
     return int(n)
@@ -222,17 +228,9 @@ def decode_auto_split(B: int, Hq: int, Hkv: int, d: int, max_ctx: int) -> int:
     return int(ks)
 
 
-def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: Optional[torch.Tensor] = None, *,
-           cu_seqlens: Optional[torch.Tensor] = None, max_ctx: Optional[int] = None,
-           num_kv_heads: Optional[int] = None, scale: Optional[float] = None, keys_per_split: int = 0,
-           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-           stream=None) -> torch.Tensor:
-    """Parallax decode: one query token per sequence.  q, rho: [B, Hq, d].
-
-    Contiguous cache: k_cache, v_cache [B, Hkv, L, d] (cu_seqlens None).
-    Ragged cache: cu_seqlens int64 [B + 1] on the GPU, k_cache / v_cache the
-    packed slabs (any shape, contiguous), num_kv_heads and max_ctx required.
-    """
+def _decode_args(q, k_cache, v_cache, rho, cu_seqlens, max_ctx, num_kv_heads, scale, out):
+    """Shape checks shared by the decode entry points; returns the marshalled
+    sizes and the output tensor."""
     if q.dim() != 3:
         raise ValueError("q must be [B, Hq, d]")
     B, Hq, d = q.shape
@@ -260,17 +258,59 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: O
     elif out.shape != q.shape:
         raise ValueError("out must have q's shape")
     _check_tensors(q.dtype, q=q, rho=rho, k_cache=k_cache, v_cache=v_cache, out=out)
+    _check_device(q=q, cu_seqlens=cu_seqlens)
     code = _dtype_code(q.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return B, Hq, Hkv, d, int(max_ctx), out, code, scale
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: Optional[torch.Tensor] = None, *,
+           cu_seqlens: Optional[torch.Tensor] = None, max_ctx: Optional[int] = None,
+           num_kv_heads: Optional[int] = None, scale: Optional[float] = None, keys_per_split: int = 0,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Parallax decode: one query token per sequence.  q, rho: [B, Hq, d].
+
+    Contiguous cache: k_cache, v_cache [B, Hkv, L, d] (cu_seqlens None).
+    Ragged cache: cu_seqlens int64 [B + 1] on the GPU, k_cache / v_cache the
+    packed slabs (any shape, contiguous), num_kv_heads and max_ctx required.
+    keys_per_split=0 calls parallax_fwd_decode (the library chooses the
+    chunking); any other value calls parallax_fwd_decode_chunked with it.
+    """
+    B, Hq, Hkv, d, max_ctx, out, code, scale = _decode_args(q, k_cache, v_cache, rho, cu_seqlens, max_ctx,
+                                                            num_kv_heads, scale, out)
     need = decode_workspace_size(B, Hq, Hkv, d, max_ctx, q.dtype, keys_per_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
-    _check_device(q=q, cu_seqlens=cu_seqlens, workspace=workspace)
+    _check_device(q=q, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = N.load().parallax_fwd_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
-                                      int(max_ctx), _ptr(out), B, Hq, Hkv, d, scale, code, int(keys_per_split),
-                                      _ptr(workspace), ws_bytes, _stream(stream))
-    N.check(st, "parallax_fwd_decode")
+    lib = N.load()
+    args = (_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), max_ctx, _ptr(out), B, Hq,
+            Hkv, d, scale, code)
+    if keys_per_split:
+        st = lib.parallax_fwd_decode_chunked(*args, int(keys_per_split), _ptr(workspace), ws_bytes,
+                                             _stream(stream))
+        N.check(st, "parallax_fwd_decode_chunked")
+    else:
+        st = lib.parallax_fwd_decode(*args, _ptr(workspace), ws_bytes, _stream(stream))
+        N.check(st, "parallax_fwd_decode")
     return out
+
+
+# The C entry points' own names, for callers who think in terms of the ABI.
+parallax_fwd_prefill = prefill
+parallax_fwd_prefill_train = prefill_train
+parallax_bwd_prefill = prefill_backward
+parallax_qkvr_projection = qkvr_projection
+parallax_fwd_decode = decode
+parallax_fwd_decode_workspace_size = decode_workspace_size
+parallax_fwd_decode_auto_split = decode_auto_split
+
+
+def parallax_fwd_decode_chunked(q, k_cache, v_cache, rho=None, *, keys_per_split: int, **kw):
+    """parallax_fwd_decode_chunked: decode with the caller's chunk size."""
+    if keys_per_split <= 0:
+        raise ValueError("keys_per_split must be positive (0 is parallax_fwd_decode's own choice)")
+    return decode(q, k_cache, v_cache, rho, keys_per_split=keys_per_split, **kw)

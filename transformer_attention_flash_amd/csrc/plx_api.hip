@@ -91,7 +91,7 @@ plx_status_t plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t 
 // Causal prefill forward; the training variant also keeps (out_sa, lse, rbar).
 plx_status_t prefill_impl(const void *q, const void *k, const void *v, const void *rho, void *out, void *out_sa,
                           float *lse, float *rbar, int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
-                          float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
+                          float softmax_scale, plx_dtype_t dtype, hipStream_t stream) {
     if (!q || !k || !v || !out) return PLX_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(out) ||
         !aligned16(out_sa) || !aligned16(lse) || !aligned16(rbar))
@@ -134,8 +134,57 @@ plx_status_t prefill_impl(const void *q, const void *k, const void *v, const voi
     p.T = T;
     p.n_qblk = static_cast<int32_t>(n_qblk);
     p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
-    const hipError_t e =
-        plx::launch_prefill(p, bf16, d, G, rho != nullptr, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_prefill(p, bf16, d, G, rho != nullptr, stream);
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+// Decode over the caller's workspace.
+plx_status_t decode_impl(const void *q, const void *rho, const void *k_cache, const void *v_cache,
+                         const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t d, float softmax_scale, plx_dtype_t dtype, int32_t keys_per_split, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !out) return PLX_ERR_INVALID_ARGUMENT;
+    // With max_ctx == 0 every sequence is empty and no key is read, so an
+    // empty cache may come without storage.
+    if (max_ctx != 0 && (!k_cache || !v_cache)) return PLX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(workspace) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0)
+        return PLX_ERR_INVALID_ARGUMENT;
+    plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
+    if (st != PLX_OK) return st;
+    DecodePlan plan;
+    st = plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan);
+    if (st != PLX_OK) return st;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return PLX_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t es = elem_bytes(dtype);
+    const size_t q_bytes = static_cast<size_t>(B) * Hq * d * es;
+    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, rho, q_bytes) ||
+        overlaps(out, q_bytes, workspace, plan.bytes))
+        return PLX_ERR_INVALID_ARGUMENT;
+    if (!cu_seqlens) {
+        const size_t kv_bytes = static_cast<size_t>(B) * Hkv * static_cast<size_t>(max_ctx) * d * es;
+        if (overlaps(out, q_bytes, k_cache, kv_bytes) || overlaps(out, q_bytes, v_cache, kv_bytes))
+            return PLX_ERR_INVALID_ARGUMENT;
+    }
+
+    plx::DecodeParams p;
+    p.q = q;
+    p.rho = rho;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.cu = cu_seqlens;
+    p.max_ctx = max_ctx;
+    p.out = out;
+    p.ws_stats = plan.bytes ? static_cast<float *>(workspace) : nullptr;
+    p.ws_vec = plan.bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.stats_bytes) : nullptr;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.keys_per_split = plan.keys_per_split;
+    p.n_split = plan.n_split;
+    p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    const hipError_t e = plx::launch_decode(p, dtype == PLX_DTYPE_BF16, d, Hq / Hkv, stream);
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
@@ -145,7 +194,7 @@ extern "C" {
 
 plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, const void *rho, void *out,
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
-                                  float softmax_scale, plx_dtype_t dtype, plx_stream_t stream) {
+                                  float softmax_scale, plx_dtype_t dtype, hipStream_t stream) {
     return prefill_impl(q, k, v, rho, out, nullptr, nullptr, nullptr, B, Hq, Hkv, T, d, softmax_scale, dtype,
                         stream);
 }
@@ -153,7 +202,7 @@ plx_status_t parallax_fwd_prefill(const void *q, const void *k, const void *v, c
 plx_status_t parallax_fwd_prefill_train(const void *q, const void *k, const void *v, const void *rho, void *out,
                                         void *out_sa, float *lse, float *rbar, int32_t B, int32_t Hq,
                                         int32_t Hkv, int32_t T, int32_t d, float softmax_scale,
-                                        plx_dtype_t dtype, plx_stream_t stream) {
+                                        plx_dtype_t dtype, hipStream_t stream) {
     if (!lse) return PLX_ERR_INVALID_ARGUMENT;
     if ((rho == nullptr) != (out_sa == nullptr) || (rho == nullptr) != (rbar == nullptr))
         return PLX_ERR_INVALID_ARGUMENT;
@@ -170,7 +219,7 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v, c
                                   const void *out_sa, const float *lse, const float *rbar, const void *dout,
                                   void *dq, void *dk, void *dv, void *drho, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t T, int32_t d, float softmax_scale, plx_dtype_t dtype, void *workspace,
-                                  size_t workspace_bytes, plx_stream_t stream) {
+                                  size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return PLX_ERR_INVALID_ARGUMENT;
     const bool has_rho = rho != nullptr;
     if (has_rho != (out_sa != nullptr) || has_rho != (rbar != nullptr) || has_rho != (drho != nullptr))
@@ -232,13 +281,13 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v, c
     p.n_kblk = static_cast<int32_t>(n_kblk);
     p.scale = softmax_scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
-    const hipError_t e = plx::launch_backward(p, d, G, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_backward(p, d, G, stream);
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
 plx_status_t parallax_qkvr_projection(const void *x, const void *w, void *q, void *k, void *v, void *rho,
                                       int32_t B, int32_t T, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t d,
-                                      plx_dtype_t dtype, plx_stream_t stream) {
+                                      plx_dtype_t dtype, hipStream_t stream) {
     if (!x || !w || !q || !k || !v || !rho) return PLX_ERR_INVALID_ARGUMENT;
     const void *ptrs[] = {x, w, q, k, v, rho};
     for (const void *ptr : ptrs)
@@ -284,12 +333,17 @@ plx_status_t parallax_qkvr_projection(const void *x, const void *w, void *q, voi
     p.nkv = Hkv * d;
     p.n_fblk = static_cast<int32_t>(n_fblk);
     p.n_tblk = static_cast<int32_t>(n_tblk);
-    const hipError_t e = plx::launch_projection(p, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_projection(p, stream);
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
 size_t parallax_fwd_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx,
-                                          plx_dtype_t dtype, int32_t keys_per_split) {
+                                          plx_dtype_t dtype) {
+    return parallax_fwd_decode_chunked_workspace_size(B, Hq, Hkv, d, max_ctx, dtype, 0);
+}
+
+size_t parallax_fwd_decode_chunked_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t max_ctx,
+                                                  plx_dtype_t dtype, int32_t keys_per_split) {
     DecodePlan plan;
     if (plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan) != PLX_OK) return ~size_t{0};
     return plan.bytes;
@@ -303,53 +357,19 @@ int32_t parallax_fwd_decode_auto_split(int32_t B, int32_t Hq, int32_t Hkv, int32
 
 plx_status_t parallax_fwd_decode(const void *q, const void *rho, const void *k_cache, const void *v_cache,
                                  const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B, int32_t Hq,
-                                 int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype,
-                                 int32_t keys_per_split, void *workspace, size_t workspace_bytes,
-                                 plx_stream_t stream) {
-    if (!q || !out) return PLX_ERR_INVALID_ARGUMENT;
-    // With max_ctx == 0 every sequence is empty and no key is read, so an
-    // empty cache may come without storage.
-    if (max_ctx != 0 && (!k_cache || !v_cache)) return PLX_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        !aligned16(workspace) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0)
-        return PLX_ERR_INVALID_ARGUMENT;
-    plx_status_t st = check_heads(B, Hq, Hkv, d, softmax_scale, dtype);
-    if (st != PLX_OK) return st;
-    DecodePlan plan;
-    st = plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan);
-    if (st != PLX_OK) return st;
-    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return PLX_ERR_WORKSPACE_TOO_SMALL;
+                                 int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(q, rho, k_cache, v_cache, cu_seqlens, max_ctx, out, B, Hq, Hkv, d, softmax_scale, dtype, 0,
+                       workspace, workspace_bytes, stream);
+}
 
-    const size_t es = elem_bytes(dtype);
-    const size_t q_bytes = static_cast<size_t>(B) * Hq * d * es;
-    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, rho, q_bytes) ||
-        overlaps(out, q_bytes, workspace, plan.bytes))
-        return PLX_ERR_INVALID_ARGUMENT;
-    if (!cu_seqlens) {
-        const size_t kv_bytes = static_cast<size_t>(B) * Hkv * static_cast<size_t>(max_ctx) * d * es;
-        if (overlaps(out, q_bytes, k_cache, kv_bytes) || overlaps(out, q_bytes, v_cache, kv_bytes))
-            return PLX_ERR_INVALID_ARGUMENT;
-    }
-
-    plx::DecodeParams p;
-    p.q = q;
-    p.rho = rho;
-    p.k = k_cache;
-    p.v = v_cache;
-    p.cu = cu_seqlens;
-    p.max_ctx = max_ctx;
-    p.out = out;
-    p.ws_stats = plan.bytes ? static_cast<float *>(workspace) : nullptr;
-    p.ws_vec = plan.bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.stats_bytes) : nullptr;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.keys_per_split = plan.keys_per_split;
-    p.n_split = plan.n_split;
-    p.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
-    const hipError_t e =
-        plx::launch_decode(p, dtype == PLX_DTYPE_BF16, d, Hq / Hkv, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+plx_status_t parallax_fwd_decode_chunked(const void *q, const void *rho, const void *k_cache, const void *v_cache,
+                                         const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype,
+                                         int32_t keys_per_split, void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    return decode_impl(q, rho, k_cache, v_cache, cu_seqlens, max_ctx, out, B, Hq, Hkv, d, softmax_scale, dtype,
+                       keys_per_split, workspace, workspace_bytes, stream);
 }
 
 const char *parallax_status_string(plx_status_t s) {

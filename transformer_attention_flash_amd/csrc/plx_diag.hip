@@ -77,7 +77,7 @@ plx_status_t parallax_diag_device_info(int32_t device, int32_t *cu_count, int32_
 }
 
 plx_status_t parallax_diag_stream_read(const void *src, size_t bytes, int32_t nontemporal, void *sink,
-                                       plx_stream_t stream) {
+                                       hipStream_t stream) {
     if (!src || !sink || bytes == 0 || bytes % 16 != 0) return PLX_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
         return PLX_ERR_INVALID_ARGUMENT;
@@ -93,7 +93,7 @@ plx_status_t parallax_diag_stream_read(const void *src, size_t bytes, int32_t no
     if (blocks > need) blocks = need;
     const auto *p = static_cast<const plx::u32x4 *>(src);
     auto *out = static_cast<uint32_t *>(sink);
-    auto st = static_cast<hipStream_t>(stream);
+    auto st = stream;
     if (nontemporal)
         hipLaunchKernelGGL(plx::stream_read_kernel<true>, dim3(static_cast<uint32_t>(blocks)),
                            dim3(plx::kDiagThreads), 0, st, p, n_vec, out);
@@ -103,12 +103,12 @@ plx_status_t parallax_diag_stream_read(const void *src, size_t bytes, int32_t no
     return hipGetLastError() == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-plx_status_t parallax_diag_mfma_bf16(void *sink, int32_t n_blocks, int32_t iterations, plx_stream_t stream) {
+plx_status_t parallax_diag_mfma_bf16(void *sink, int32_t n_blocks, int32_t iterations, hipStream_t stream) {
     if (!sink || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return PLX_ERR_INVALID_ARGUMENT;
     if (n_blocks < 1 || n_blocks > (1 << 20) || iterations < 1 || iterations > (1 << 24))
         return PLX_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(plx::mfma_bf16_kernel, dim3(static_cast<uint32_t>(n_blocks)), dim3(plx::kDiagThreads), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint32_t *>(sink), iterations);
+                       stream, static_cast<uint32_t *>(sink), iterations);
     return hipGetLastError() == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
