@@ -301,6 +301,33 @@ size_t parallax_fwd_decode_chunked_workspace_size(int32_t B, int32_t Hq,
                                                   plx_dtype_t dtype,
                                                   int32_t keys_per_split);
 
+/*
+ * Decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, chunking, result (bit for bit) and
+ * errors as parallax_fwd_decode, minus the workspace: the per-chunk partials
+ * go to a scratch buffer of PLX_DECODE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each device it runs on, from the first call there until the
+ * process ends.  The first call on a device resolves that buffer's address
+ * (hipGetSymbolAddress); no call allocates or frees anything.
+ *
+ * Every call on one device shares its buffer, so calls that overlap in time
+ * on one device race (two streams, or two host threads): serialise them.  A
+ * call whose workspace size (parallax_fwd_decode_workspace_size) exceeds the
+ * buffer returns PLX_ERR_WORKSPACE_TOO_SMALL before any HIP call; every
+ * contiguous or ragged cache of up to 2^20 keys fits.
+ */
+#define PLX_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+plx_status_t parallax_fwd_decode_noalloc(const void *q, const void *rho,
+                                         const void *k_cache,
+                                         const void *v_cache,
+                                         const int64_t *cu_seqlens,
+                                         int64_t max_ctx, void *out, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d,
+                                         float softmax_scale, plx_dtype_t dtype,
+                                         hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char *parallax_status_string(plx_status_t s);
 

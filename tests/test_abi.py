@@ -173,6 +173,36 @@ def test_decode_chunked_rejections(lib, kw, code):
     assert decode(lib, **{"ks": 256, **kw}) == code
 
 
+def decode_noalloc(lib, q=P[0], rho=P[1], k=P[2], v=P[3], cu=None, max_ctx=4096, out=P[4], B=2, Hq=4, Hkv=2,
+                   d=128, scale=0.088, dtype=BF16):
+    return lib.parallax_fwd_decode_noalloc(q, rho, k, v, cu, max_ctx, out, B, Hq, Hkv, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (kw, code) for kw, code in DECODE_REJECTIONS if "ws" not in kw and "ws_bytes" not in kw and kw != dict(out=P[5])
+] + [
+    # 64 sequences x 8 KV heads of 2^22 keys: 4 chunks of 2^20 keys each, whose partials
+    # (64 x 64 heads x 4 chunks x 1036 B) exceed the fixed scratch
+    (dict(B=64, Hq=64, Hkv=8, max_ctx=1 << 22), WS),
+])
+def test_decode_noalloc_rejections(lib, kw, code):
+    """Every rejection happens in the host checks, before the first HIP call
+    (this machine has no GPU, so a call that got further would fail with
+    PLX_ERR_HIP instead)."""
+    assert decode_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_limit_matches_header(lib):
+    text = open(os.path.join(ROOT, "include", "parallax.h")).read()
+    assert "#define PLX_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert N.DECODE_NOALLOC_SCRATCH_BYTES == 16 << 20
+    # the largest split the library's own chunking picks for caches of up to 2^20 keys fits
+    f = lib.parallax_fwd_decode_workspace_size
+    worst = max(f(B, 8 * Hkv, Hkv, 128, L, BF16) for B in (1, 2, 3, 5, 7, 33, 63) for Hkv in (1, 3, 8, 64)
+                for L in (257, 4097, 65537, 1 << 20))
+    assert 0 < worst <= N.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_workspace_size(lib):
     f = lib.parallax_fwd_decode_workspace_size
     fc = lib.parallax_fwd_decode_chunked_workspace_size

@@ -19,6 +19,10 @@ PLX_ERR_HIP = 4
 PLX_DTYPE_F32 = 0
 PLX_DTYPE_BF16 = 1
 
+# Bytes of the per-device scratch of parallax_fwd_decode_noalloc
+# (PLX_DECODE_NOALLOC_SCRATCH_BYTES in include/parallax.h).
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
 # Every symbol include/parallax.h declares.
 EXPORTS = (
     "parallax_fwd_prefill",
@@ -31,6 +35,7 @@ EXPORTS = (
     "parallax_fwd_decode_auto_split",
     "parallax_fwd_decode_chunked",
     "parallax_fwd_decode_chunked_workspace_size",
+    "parallax_fwd_decode_noalloc",
     "parallax_status_string",
     "parallax_diag_device_info",
     "parallax_diag_stream_read",
@@ -81,6 +86,9 @@ def load():
     lib.parallax_fwd_decode_chunked.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32,
                                                 ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.parallax_fwd_decode_chunked.restype = ctypes.c_int
+    lib.parallax_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, f32,
+                                                ctypes.c_int, vp]
+    lib.parallax_fwd_decode_noalloc.restype = ctypes.c_int
     lib.parallax_fwd_decode_auto_split.argtypes = [i32, i32, i32, i32, i64]
     lib.parallax_fwd_decode_auto_split.restype = i32
     lib.parallax_status_string.argtypes = [ctypes.c_int]

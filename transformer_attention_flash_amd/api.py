@@ -299,6 +299,21 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, rho: O
     return out
 
 
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   rho: Optional[torch.Tensor] = None, *, cu_seqlens: Optional[torch.Tensor] = None,
+                   max_ctx: Optional[int] = None, num_kv_heads: Optional[int] = None,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """parallax_fwd_decode_noalloc: decode whose split partials go to the
+    library's own per-device scratch, so the call allocates nothing (pass
+    `out` to allocate nothing here either).  Arguments as decode()."""
+    B, Hq, Hkv, d, max_ctx, out, code, scale = _decode_args(q, k_cache, v_cache, rho, cu_seqlens, max_ctx,
+                                                            num_kv_heads, scale, out)
+    st = N.load().parallax_fwd_decode_noalloc(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
+                                              max_ctx, _ptr(out), B, Hq, Hkv, d, scale, code, _stream(stream))
+    N.check(st, "parallax_fwd_decode_noalloc")
+    return out
+
+
 # The C entry points' own names, for callers who think in terms of the ABI.
 parallax_fwd_prefill = prefill
 parallax_fwd_prefill_train = prefill_train
@@ -307,6 +322,7 @@ parallax_qkvr_projection = qkvr_projection
 parallax_fwd_decode = decode
 parallax_fwd_decode_workspace_size = decode_workspace_size
 parallax_fwd_decode_auto_split = decode_auto_split
+parallax_fwd_decode_noalloc = decode_noalloc
 
 
 def parallax_fwd_decode_chunked(q, k_cache, v_cache, rho=None, *, keys_per_split: int, **kw):

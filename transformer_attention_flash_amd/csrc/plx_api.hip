@@ -4,8 +4,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/parallax.h"
 #include "plx_kernels.h"
+
+// Scratch of parallax_fwd_decode_noalloc: the per-chunk partial results of a
+// split decode, for callers that cannot allocate.  Each device holds its own
+// copy from the first call on it until the process ends.  In host code this
+// name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below) and is the only form passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[PLX_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -138,11 +148,39 @@ plx_status_t prefill_impl(const void *q, const void *k, const void *v, const voi
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-// Decode over the caller's workspace.
+// Device address of `scratch` on the device that runs `stream` (its own copy
+// per device), resolved once per device with that device current.  The only
+// HIP calls are the device queries and, on a device's first use,
+// hipGetSymbolAddress; nothing is allocated here.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+plx_status_t noalloc_scratch(hipStream_t stream, void **ptr) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return PLX_ERR_HIP;
+    dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return PLX_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return PLX_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return PLX_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return PLX_ERR_HIP;
+        if (e != hipSuccess || p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return PLX_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PLX_OK;
+}
+
+// Decode; with use_scratch the partials go to the library's static scratch
+// instead of the caller's workspace (workspace / workspace_bytes unused).
 plx_status_t decode_impl(const void *q, const void *rho, const void *k_cache, const void *v_cache,
                          const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B, int32_t Hq, int32_t Hkv,
                          int32_t d, float softmax_scale, plx_dtype_t dtype, int32_t keys_per_split, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
     if (!q || !out) return PLX_ERR_INVALID_ARGUMENT;
     // With max_ctx == 0 every sequence is empty and no key is read, so an
     // empty cache may come without storage.
@@ -155,7 +193,13 @@ plx_status_t decode_impl(const void *q, const void *rho, const void *k_cache, co
     DecodePlan plan;
     st = plan_decode(B, Hq, Hkv, d, max_ctx, dtype, keys_per_split, &plan);
     if (st != PLX_OK) return st;
-    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return PLX_ERR_WORKSPACE_TOO_SMALL;
+    if (use_scratch) {
+        if (plan.bytes > PLX_DECODE_NOALLOC_SCRATCH_BYTES) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        workspace = nullptr;
+        workspace_bytes = 0;
+    } else if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) {
+        return PLX_ERR_WORKSPACE_TOO_SMALL;
+    }
 
     const size_t es = elem_bytes(dtype);
     const size_t q_bytes = static_cast<size_t>(B) * Hq * d * es;
@@ -166,6 +210,12 @@ plx_status_t decode_impl(const void *q, const void *rho, const void *k_cache, co
         const size_t kv_bytes = static_cast<size_t>(B) * Hkv * static_cast<size_t>(max_ctx) * d * es;
         if (overlaps(out, q_bytes, k_cache, kv_bytes) || overlaps(out, q_bytes, v_cache, kv_bytes))
             return PLX_ERR_INVALID_ARGUMENT;
+    }
+
+    // Every argument check is done; only now may HIP be called.
+    if (use_scratch && plan.bytes > 0) {
+        st = noalloc_scratch(stream, &workspace);
+        if (st != PLX_OK) return st;
     }
 
     plx::DecodeParams p;
@@ -370,6 +420,14 @@ plx_status_t parallax_fwd_decode_chunked(const void *q, const void *rho, const v
                                          hipStream_t stream) {
     return decode_impl(q, rho, k_cache, v_cache, cu_seqlens, max_ctx, out, B, Hq, Hkv, d, softmax_scale, dtype,
                        keys_per_split, workspace, workspace_bytes, stream);
+}
+
+plx_status_t parallax_fwd_decode_noalloc(const void *q, const void *rho, const void *k_cache, const void *v_cache,
+                                         const int64_t *cu_seqlens, int64_t max_ctx, void *out, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d, float softmax_scale, plx_dtype_t dtype,
+                                         hipStream_t stream) {
+    return decode_impl(q, rho, k_cache, v_cache, cu_seqlens, max_ctx, out, B, Hq, Hkv, d, softmax_scale, dtype, 0,
+                       nullptr, 0, stream, true);
 }
 
 const char *parallax_status_string(plx_status_t s) {
