@@ -214,20 +214,100 @@ def test_grouped_selection_matches_full(oracle_mod):
         assert np.array_equal(dk, full[1][b, g]) and np.array_equal(dv, full[2][b, g])
 
 
-def test_forward_stats_match_forward_oracle(oracle_mod):
-    """forward_stats' o^SA equals the forward oracle with a zero probe, and its
-    lse2 and rbar satisfy their definitions on a hand check."""
-    B, Hq, Hkv, T, d = 1, 2, 1, 5, 3
-    q, k, v, rho, _ = _make(22, B, Hq, Hkv, T, d)
+# --------------------------------------------------------------------------
+# forward_stats: the row statistics the training forward keeps (lse2, rbar,
+# o^SA), pinned by closed forms, an independent brute force and the C oracle
+# --------------------------------------------------------------------------
+
+def fstat_pin_zero_query(m):
+    """q = 0: every score is 0, so lse2 = log2(t + 1) exactly and the weights
+    are uniform: rbar = mean_j <k_j, rho>, o^SA = mean_j v_j (GQA, Hkv = 2)."""
+    B, Hq, Hkv, T, d = 1, 4, 2, 6, 3
+    _, k, v, rho, _ = _make(30, B, Hq, Hkv, T, d, rho_scale=1.0)
+    q = np.zeros((B, Hq, T, d))
     rows = np.array([[0, h, t] for h in range(Hq) for t in range(T)])
-    lse2, rbar, o_sa = ograd.forward_stats(q, k, v, rho, 0.5, rows)
-    assert np.allclose(o_sa, oracle.prefill(q, k, v, None, 0.5, rows=rows), atol=1e-14, rtol=0)
-    b, h, t = 0, 1, 3
-    s = 0.5 * (k[0, 0, :t + 1] @ q[b, h, t])
-    n = h * T + t
-    assert abs(lse2[n] - math.log2(np.exp(s).sum())) < 1e-12
-    p = np.exp(s) / np.exp(s).sum()
-    assert abs(rbar[n] - p @ (k[0, 0, :t + 1] @ rho[b, h, t])) < 1e-12
+    lse2, rbar, o_sa = m.forward_stats(q, k, v, rho, 0.7, rows)
+    ok = True
+    for n, (_, h, t) in enumerate(rows):
+        kv = h // (Hq // Hkv)
+        ok &= abs(lse2[n] - math.log2(t + 1)) < 1e-13
+        ok &= abs(rbar[n] - float(np.mean(k[0, kv, :t + 1] @ rho[0, h, t]))) < 1e-13
+        ok &= bool(np.abs(o_sa[n] - v[0, kv, :t + 1].mean(axis=0)).max() < 1e-13)
+    return ok
+
+
+def fstat_pin_one_key(m):
+    """Row t = 0 has one key: lse2 = s_0 log2 e with s_0 = tau q.k_0,
+    rbar = <k_0, rho>, o^SA = v_0."""
+    B, Hq, Hkv, T, d = 2, 4, 2, 3, 5
+    q, k, v, rho, _ = _make(31, B, Hq, Hkv, T, d)
+    tau = 0.45
+    rows = np.array([[b, h, 0] for b in range(B) for h in range(Hq)])
+    lse2, rbar, o_sa = m.forward_stats(q, k, v, rho, tau, rows)
+    ok = True
+    for n, (b, h, _) in enumerate(rows):
+        k0 = k[b, h // (Hq // Hkv), 0]
+        ok &= abs(lse2[n] - tau * float(q[b, h, 0] @ k0) * math.log2(math.e)) < 1e-12
+        ok &= abs(rbar[n] - float(rho[b, h, 0] @ k0)) < 1e-12
+        ok &= bool(np.abs(o_sa[n] - v[b, h // (Hq // Hkv), 0]).max() < 1e-14)
+    return ok
+
+
+def _brute_stats(q, k, v, rho, tau, b, h, t, G):
+    """Plain loops with the math module: lse2, rbar and o^SA of one row."""
+    d = len(q[b, h, t])
+    g = h // G
+    s = [tau * sum(q[b, h, t, a] * k[b, g, j, a] for a in range(d)) for j in range(t + 1)]
+    top = max(s)
+    e = [math.exp(x - top) for x in s]
+    z = sum(e)
+    lse2 = (top + math.log(z)) / math.log(2.0)
+    r = [sum(rho[b, h, t, a] * k[b, g, j, a] for a in range(d)) for j in range(t + 1)]
+    rbar = sum(e[j] / z * r[j] for j in range(t + 1))
+    osa = [sum(e[j] / z * v[b, g, j, a] for j in range(t + 1)) for a in range(d)]
+    return lse2, rbar, osa
+
+
+def fstat_pin_brute_force_gqa(m):
+    """Every row of a GQA case (Hq = 4, Hkv = 2) against plain loops."""
+    B, Hq, Hkv, T, d = 2, 4, 2, 5, 3
+    q, k, v, rho, _ = _make(32, B, Hq, Hkv, T, d, rho_scale=0.8)
+    tau = 0.6
+    rows = np.array([[b, h, t] for b in range(B) for h in range(Hq) for t in range(T)])
+    lse2, rbar, o_sa = m.forward_stats(q, k, v, rho, tau, rows)
+    ok = True
+    for n, (b, h, t) in enumerate(rows):
+        l2, rb, osa = _brute_stats(q, k, v, rho, tau, b, h, t, Hq // Hkv)
+        ok &= abs(lse2[n] - l2) < 1e-12 and abs(rbar[n] - rb) < 1e-12
+        ok &= bool(np.abs(o_sa[n] - np.array(osa)).max() < 1e-12)
+    return ok
+
+
+def fstat_pin_c_oracle_gqa(m):
+    """Against the C forward oracle (independent code, GQA with Hkv = 2):
+    o^SA is its output with a zero probe, and rbar_i is its softmax output
+    for a value column that holds r_j = <rho_i, k_j> (the softmax average of
+    r is rbar by definition)."""
+    B, Hq, Hkv, T, d = 1, 4, 2, 7, 4
+    q, k, v, rho, _ = _make(33, B, Hq, Hkv, T, d)
+    rows = np.array([[0, h, t] for h in range(Hq) for t in range(T)])
+    lse2, rbar, o_sa = m.forward_stats(q, k, v, rho, 0.5, rows)
+    ok = bool(np.abs(o_sa - oracle.prefill(q, k, v, None, 0.5, rows=rows)).max() < 1e-13)
+    for n, (_, h, t) in enumerate(rows):
+        G = Hq // Hkv
+        vr = np.zeros_like(v)
+        vr[0, h // G, :, 0] = k[0, h // G] @ rho[0, h, t]
+        want = oracle.prefill(q, k, vr, None, 0.5, rows=rows[n:n + 1])[0, 0]
+        ok &= abs(rbar[n] - want) < 1e-13
+    return ok
+
+
+FSTAT_PINS = [fstat_pin_zero_query, fstat_pin_one_key, fstat_pin_brute_force_gqa, fstat_pin_c_oracle_gqa]
+
+
+@pytest.mark.parametrize("pin", FSTAT_PINS, ids=[p.__name__ for p in FSTAT_PINS])
+def test_forward_stats_pin(oracle_mod, pin):
+    assert pin(ograd)
 
 
 # --------------------------------------------------------------------------
@@ -267,3 +347,28 @@ def test_planted_mistakes_are_caught(oracle_mod, name):
     failed = [p.__name__ for p in PINS if not p(mod)]
     print(f"{name}: caught by {len(failed)} pin(s): {failed}")
     assert failed, f"planted mistake '{name}' passes every pin"
+
+
+FSTAT_MUTATIONS = {
+    "forward_stats: KV head h % Hkv": ("kk = k[b, h // G, :t + 1]", "kk = k[b, h % (q.shape[1] // G), :t + 1]"),
+    "forward_stats: natural-log lse": ("lse2[n] = (m + np.log(e.sum())) / np.log(2.0)", "lse2[n] = m + np.log(e.sum())"),
+    "forward_stats: unnormalised weights in rbar": ("rbar[n] = p @ (kk @ rho[b, h, t])",
+                                                    "rbar[n] = e @ (kk @ rho[b, h, t])"),
+    "forward_stats: lse without the max": ("lse2[n] = (m + np.log(e.sum())) / np.log(2.0)",
+                                           "lse2[n] = np.log(e.sum()) / np.log(2.0)"),
+    "forward_stats: o^SA from the wrong KV head": ("o_sa[n] = p @ v[b, h // G, :t + 1]",
+                                                   "o_sa[n] = p @ v[b, (h // G + 1) % (q.shape[1] // G), :t + 1]"),
+    "forward_stats: scale dropped": ("s = tau * (kk @ q[b, h, t])", "s = kk @ q[b, h, t]"),
+}
+
+
+@pytest.mark.parametrize("name", list(FSTAT_MUTATIONS))
+def test_planted_forward_stats_mistakes_are_caught(oracle_mod, name):
+    old, new = FSTAT_MUTATIONS[name]
+    src = open(GRAD_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mod = types.ModuleType("grad_fstat_mutant")
+    exec(compile(src.replace(old, new), GRAD_SRC + " (mutant)", "exec"), mod.__dict__)
+    failed = [p.__name__ for p in FSTAT_PINS if not p(mod)]
+    print(f"{name}: caught by {len(failed)} pin(s): {failed}")
+    assert failed, f"planted mistake '{name}' passes every forward_stats pin"
