@@ -12,7 +12,7 @@ import oracle
 import transformer_attention_flash_amd as plx
 from transformer_attention_flash_amd import synth
 
-from gpu_common import assert_close, assert_close_scaled, host64, say
+from gpu_common import assert_close, assert_within_bound, bound_decode, bound_prefill, host64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -211,8 +211,10 @@ def test_prefill_sharp_scores(dtype):
     x["k"][:, :, 450, :] = x["q"][:, 0::2, 450, :] / 8  # key 450 of KV head g aligned with query head 2g
     out = plx.prefill(x["q"], x["k"], x["v"], x["rho"])
     torch.cuda.synchronize()
-    ref = oracle.prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["rho"]), _tau(d))
-    assert_close_scaled(host64(out), ref, dtype, f"prefill sharp {dtype}")
+    h = {n: host64(x[n]) for n in ("q", "k", "v", "rho")}
+    ref = oracle.prefill(h["q"], h["k"], h["v"], h["rho"], _tau(d))
+    bound = bound_prefill(h["q"], h["k"], h["v"], h["rho"], _tau(d), dtype)
+    assert_within_bound(host64(out), ref, bound, f"prefill sharp {dtype}")
 
 
 def test_decode_sharp_scores():
@@ -222,11 +224,13 @@ def test_decode_sharp_scores():
     x = synth.make_decode(2, 8, 4, 3000, 128, BF, DEV, seed=9)
     x["q"] = x["q"] * 8
     x["k"][:, :, 2900, :] = x["q"][:, 0::2, :] / 8
-    ref = oracle.decode(host64(x["q"]), host64(x["rho"]), host64(x["k"]), host64(x["v"]), _tau(128))
+    h = {n: host64(x[n]) for n in ("q", "k", "v", "rho")}
+    ref = oracle.decode(h["q"], h["rho"], h["k"], h["v"], _tau(128))
     for ks in (0, 256):
         out = plx.decode(x["q"], x["k"], x["v"], x["rho"], keys_per_split=ks)
         torch.cuda.synchronize()
-        assert_close_scaled(host64(out), ref, BF, f"decode sharp ks={ks}")
+        bound = bound_decode(h["q"], h["rho"], h["k"], h["v"], _tau(128), BF, n_merge=1 if ks == 0 else 2)
+        assert_within_bound(host64(out), ref, bound, f"decode sharp ks={ks}")
 
 
 def test_prefill_deterministic():

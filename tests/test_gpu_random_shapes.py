@@ -6,8 +6,9 @@ size, length, head dimension, dtype, chunk size and a softmax scale away from
 1/sqrt(d), so that a kernel that ignored the scale argument, or mishandled an
 odd length or head count, fails.  Every output element is compared with the
 fp64 oracle.  Short contexts give outputs of size O(1) rather than the O(0.1)
-averages of the standard workloads, so the bar is the per-element bound of
-assert_close_scaled (output rounding and operand rounding scale with |o|).
+averages of the standard workloads, so the bar is each element's first-order
+rounding bound (gpu_common._rows_bound: operand, score and output rounding)
+and rel-L2 5e-3.
 """
 import math
 
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import assert_close_scaled, errors, gpu_available, host64, say
+from gpu_common import assert_within_bound, bound_decode, bound_prefill, errors, gpu_available, host64, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -81,8 +82,9 @@ def test_prefill_random_shape(case):
     out = plx.prefill(x["q"], x["k"], x["v"], r, scale=scale)
     torch.cuda.synchronize()
     h = {k: host64(v) for k, v in x.items()}
-    ref = oracle.prefill(h["q"], h["k"], h["v"], h["rho"] if rho else np.zeros_like(h["q"]), scale)
-    assert_close_scaled(host64(out), ref, dtype, "prefill")
+    r64 = h["rho"] if rho else np.zeros_like(h["q"])
+    ref = oracle.prefill(h["q"], h["k"], h["v"], r64, scale)
+    assert_within_bound(host64(out), ref, bound_prefill(h["q"], h["k"], h["v"], r64, scale, dtype), "prefill")
 
 
 @pytest.mark.parametrize("case", DECODE, ids=[f"d{i}" for i in range(len(DECODE))])
@@ -102,9 +104,11 @@ def test_decode_random_shape(case):
     r = x["rho"] if rho else None
     out = plx.decode(x["q"], x["k"], x["v"], r, scale=scale, keys_per_split=ks, **kw)
     torch.cuda.synchronize()
-    q64, rho64 = host64(x["q"]), host64(x["rho"])
-    ref = oracle.decode(q64, rho64 if rho else np.zeros_like(q64), host64(x["k"]), host64(x["v"]), scale, **okw)
-    assert_close_scaled(host64(out), ref, dtype, "decode")
+    q64, rho64, k64, v64 = host64(x["q"]), host64(x["rho"]), host64(x["k"]), host64(x["v"])
+    r64 = rho64 if rho else np.zeros_like(q64)
+    ref = oracle.decode(q64, r64, k64, v64, scale, **okw)
+    bound = bound_decode(q64, r64, k64, v64, scale, dtype, n_merge=1 if ks == 0 else 2, **okw)
+    assert_within_bound(host64(out), ref, bound, "decode")
 
 
 BACKWARD = [
