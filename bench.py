@@ -13,7 +13,11 @@ fused q/k/v/probe projection of the same layer under "prefill"/"projection"
 only (skipped with --no-context), "prefill"/"longer_sequence" times the same heads and token count at a
 4x longer sequence (B=2, T=16384), and "decode_other_workloads" the two decode
 extremes (2048 x 128 keys, 256 x 32768 keys) and the ragged batch (2048
-sequences of 128..32768 keys, Hq=32, Hkv=16, d=64).
+sequences of 128..32768 keys, Hq=32, Hkv=16, d=64).  "prefill_f32" times the
+fp32 causal prefill (B=1, Hq=Hkv=2, T=256, d=64) and checks every row against
+the oracle.  "sweep" (skipped with --no-sweep) is the decode sweep of Parallax
+against the library's softmax-only path over batch 1..2048 x context
+128..32768, I/O-matched (same d) and compute-matched (Parallax at d=64).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Several input sets are rotated so that no step finds its K/V in the 256 MB
@@ -60,6 +64,42 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu() -> dict:
+    """The host's CPU model and the threads this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def build_info() -> dict:
+    """Git revision the library was built from (written by the build step)."""
+    path = os.path.join(ROOT, "transformer_attention_flash_amd", "_build_info.json")
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {"git_sha": None}
+
+
+def parity_errors(got, ref) -> dict:
+    """max-abs and relative L2 of the GPU rows against the oracle's."""
+    import numpy as np
+    diff = got - ref
+    return {"rows": int(got.reshape(-1, got.shape[-1]).shape[0]), "max_abs": float(np.abs(diff).max()),
+            "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
+
+
 def source_digest(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -99,10 +139,11 @@ def time_steps(fn_for_step, steps, warmup, torch):
     return evs[0].elapsed_time(evs[-1]) / 1e3, per
 
 
-def cpu_baseline_decode(x, w, budget_s: float):
+def cpu_baseline_decode(x, w, budget_s: float, gpu_out=None):
     """Oracle (expanded form) on whole sequences of the decode workload, in
     passes over the batch, until about budget_s seconds of CPU work; returns
-    the oracle's KV GB/s."""
+    the oracle's KV GB/s, and (given the GPU output on the same inputs) the
+    GPU's errors against the oracle rows of the first pass."""
     import numpy as np
     import oracle  # the CPU baseline leg of the benchmark
 
@@ -113,13 +154,16 @@ def cpu_baseline_decode(x, w, budget_s: float):
         sl = slice(b, min(b + 8, w.B))
         chunks.append(tuple(x[n][sl].float().cpu().numpy().astype(np.float64) for n in ("q", "rho", "k", "v")))
     done_bytes, spent, nseq, passes = 0, 0.0, 0, 0
+    first = []
     while spent < budget_s:
         for q, r, k, v in chunks:
             t0 = time.perf_counter()
-            oracle.decode(q, r, k, v, tau, form=oracle.EXPANDED)
+            o = oracle.decode(q, r, k, v, tau, form=oracle.EXPANDED)
             spent += time.perf_counter() - t0
             nseq += q.shape[0]
             done_bytes += q.shape[0] * per_seq_bytes
+            if passes == 0:
+                first.append(o)
         passes += 1
     # The explicit form (a d x d covariance per row, O(L d^2)) on its own,
     # smaller sample: whole sequences until about a quarter of the budget.
@@ -133,28 +177,36 @@ def cpu_baseline_decode(x, w, budget_s: float):
             e_spent += time.perf_counter() - t0
             e_seq += 1
             e_bytes += per_seq_bytes
-    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{passes} pass(es) over all {w.B} sequences ({w.Hq} heads, {w.L} keys each; {nseq} "
-                      f"sequence evaluations), fp64 expanded form, {spent:.1f} s",
-            "explicit_form": {"value": e_bytes / e_spent / 1e9, "unit": "GB/s",
-                              "sample": f"{e_seq} whole sequence(s), fp64 explicit covariance form, {e_spent:.1f} s"}}
+    res = {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{passes} pass(es) over all {w.B} sequences ({w.Hq} heads, {w.L} keys each; {nseq} "
+                     f"sequence evaluations), fp64 expanded form, {spent:.1f} s",
+           "host": host_cpu(),
+           "explicit_form": {"value": e_bytes / e_spent / 1e9, "unit": "GB/s",
+                             "sample": f"{e_seq} whole sequence(s), fp64 explicit covariance form, {e_spent:.1f} s"}}
+    if gpu_out is not None:
+        res["gpu_parity_vs_oracle"] = parity_errors(gpu_out.float().cpu().numpy().astype(np.float64),
+                                                    np.concatenate(first))
+    return res
 
 
-def cpu_baseline_prefill(x, w, budget_s: float):
+def cpu_baseline_prefill(x, w, budget_s: float, gpu_out=None):
     """Oracle on query rows of the prefill workload (whole sequences, all
     heads, positions visited in a strided order) until about budget_s seconds;
     returns the oracle's TFLOP/s under the GPU's flop count (8 d flops per
-    causal pair)."""
+    causal pair), and (given the GPU output on the same inputs) the GPU's
+    errors against every oracle row evaluated."""
     import numpy as np
     import oracle
 
     tau = 1.0 / math.sqrt(w.d)
     flops, spent, nrows, nseq = 0.0, 0.0, 0, 0
+    got_rows, ref_rows = [], []
     step = 64
     for b in range(w.B):
         if spent >= budget_s:
             break
         q, r, k, v = (x[n][b:b + 1].float().cpu().numpy().astype(np.float64) for n in ("q", "rho", "k", "v"))
+        ob = None if gpu_out is None else gpu_out[b].float().cpu().numpy().astype(np.float64)
         nseq += 1
         for off in range(step):
             if spent >= budget_s:
@@ -162,13 +214,20 @@ def cpu_baseline_prefill(x, w, budget_s: float):
             ts = np.arange(off, w.T, step)
             rows = np.array([(0, h, t) for h in range(w.Hq) for t in ts], dtype=np.int64)
             t0 = time.perf_counter()
-            oracle.prefill(q, k, v, r, tau, form=oracle.EXPANDED, rows=rows)
+            o = oracle.prefill(q, k, v, r, tau, form=oracle.EXPANDED, rows=rows)
             spent += time.perf_counter() - t0
             nrows += len(rows)
             flops += float(8 * w.d * (rows[:, 2] + 1).sum())
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{nrows} query rows from {nseq} sequence(s) (all {w.Hq} heads, positions over "
-                      f"0..{w.T - 1}), fp64 expanded form, {spent:.1f} s"}
+            if ob is not None:
+                ref_rows.append(o)
+                got_rows.append(ob[rows[:, 1], rows[:, 2]])
+    res = {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{nrows} query rows from {nseq} sequence(s) (all {w.Hq} heads, positions over "
+                     f"0..{w.T - 1}), fp64 expanded form, {spent:.1f} s",
+           "host": host_cpu()}
+    if got_rows:
+        res["gpu_parity_vs_oracle"] = parity_errors(np.concatenate(got_rows), np.concatenate(ref_rows))
+    return res
 
 
 def cpu_baseline_backward(x, dout, w):
@@ -247,92 +306,154 @@ def measure_device(torch):
             "measured": measured}
 
 
-def run_sweep(args, torch, plx, synth):
+SWEEP_BATCHES = (1, 16, 128, 1024, 2048)
+SWEEP_CONTEXTS = (128, 1024, 8192, 32768)
+FLUSH_BYTES = 512 << 20
+SWEEP_MAX_KV_BYTES = 160 * 10 ** 9  # one input set of K/V beside the rest of the bench in 288 GB of HBM
+
+
+def run_sweep(torch, plx, synth, diag, budget_s: float):
     """Decode sweep, Parallax against the softmax-only path (rho = NULL) of the
-    same library: batch x context over the pages' range (batch 1..2048,
-    context 128..32768), Hq = 16, Hkv = 8, bf16.  Two settings:
+    same library, over the pages' range: batch 1..2048 x context 128..32768
+    (every point), Hq = 16, Hkv = 8, bf16.  Two settings:
       I/O-matched:     Parallax and softmax-only at the same d = 128;
       compute-matched: Parallax at d = 64 against softmax-only at d = 128
                        (equal matrix flops per key: Parallax has two scoring
                        and two value products, softmax attention one each).
-    Points whose eager call takes under 50 us are also timed as 64 calls
-    replayed from one HIP graph (the *_graph_* fields).  Prints one JSON line
-    per grid point."""
+    No timed call finds its K/V in the caches (4 MB L2 per XCD, 256 MB
+    Infinity Cache): points with at least 128 MB of K/V rotate enough input
+    sets to cover 512 MB; smaller points time each call alone, after a
+    cached streaming read of a 512 MB buffer that evicts them.  Points are
+    visited small to large; once budget_s is spent, the remaining points are
+    listed as skipped, as is a point whose d = 128 K/V exceeds 160 GB (2048 x
+    32768 keys: 275 GB).  Returns {"points": [...], ...}."""
     dev = "cuda"
-    grid = [(b, l) for b in (1, 16, 128, 1024, 2048) for l in (128, 1024, 8192, 32768) if b * l <= 1 << 23]
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_start = time.time()
+    points, skipped = [], []
 
-    def timed(fn, nbytes):
-        for _ in range(10):
-            fn()
+    def time_point(B, L, d, with_rho, xs_cache):
+        kv = 4 * B * 8 * L * d
+        key = (B, L, d)
+        if key not in xs_cache:
+            xs_cache.clear()
+            torch.cuda.empty_cache()
+            n_sets = 1 if kv >= FLUSH_BYTES else (-(-FLUSH_BYTES // kv) if kv >= (128 << 20) else 1)
+            xs_cache[key] = [synth.make_decode(B, 16, 8, L, d, torch.bfloat16, dev, seed=s) for s in range(n_sets)]
+        xs = xs_cache[key]
+        out = torch.empty_like(xs[0]["q"])
+        ws_n = plx.decode_workspace_size(B, 16, 8, d, L)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+        def call(i):
+            x = xs[i % len(xs)]
+            plx.decode(x["q"], x["k"], x["v"], x["rho"] if with_rho else None, out=out, workspace=ws)
+
+        for i in range(3):
+            call(i)
         torch.cuda.synchronize()
-        iters = max(5, min(200, int(3e-3 / max(nbytes / 6e12, 2e-6))))
-        best = None
-        for _ in range(3):
+        if kv >= (128 << 20):  # rotated sets, back-to-back calls between two events
+            iters = max(4 * len(xs), min(60, int(0.05 / (kv / 5e12))))
+            secs, _ = time_steps(call, iters, 0, torch)
+            return secs / iters * 1e6, len(xs), "rotated input sets"
+        per = []
+        for i in range(15):  # one call at a time after a cache-evicting read
+            diag.stream_read(flush, nontemporal=False, sink=sink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(iters):
-                fn()
+            call(i)
             e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) / iters * 1e3
-            best = t if best is None or t < best else best
-        return best
-
-    def graph_timed(fn, n_calls=64):
-        # n_calls calls captured in one HIP graph and replayed: the per-call
-        # time without the host's launch overhead, which dominates small
-        # decode steps launched one by one.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
+            per.append((e0, e1))
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for _ in range(n_calls):
-                fn()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(5):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) / (5 * n_calls) * 1e3
-            best = t if best is None or t < best else best
-        del g
-        return best
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in per)
+        return us[len(us) // 2], 1, "cache evicted before each call (median of 15)"
 
-    for B, L in grid:
-        row = {"B": B, "context": L}
-        for name, d, with_rho in (("parallax_d128", 128, True), ("softmax_d128", 128, False),
-                                  ("parallax_d64", 64, True)):
-            x = synth.make_decode(B, 16, 8, L, d, torch.bfloat16, dev, seed=0)
-            out = torch.empty_like(x["q"])
-            rho = x["rho"] if with_rho else None
-            ws = torch.empty(max(plx.decode_workspace_size(B, 16, 8, d, L), 1), dtype=torch.uint8, device=dev)
-            nbytes = 4 * B * 8 * L * d
+    xs_cache = {}
+    for L in SWEEP_CONTEXTS:
+        for B in SWEEP_BATCHES:
+            if time.time() - t_start > budget_s:
+                skipped.append({"B": B, "context": L, "reason": "time budget spent"})
+                continue
+            if 4 * B * 8 * L * 128 > SWEEP_MAX_KV_BYTES:
+                skipped.append({"B": B, "context": L, "reason": f"K/V of {4 * B * 8 * L * 128 / 1e9:.0f} GB at "
+                                                                 f"d = 128 does not fit beside the rest in HBM"})
+                continue
+            row = {"B": B, "context": L}
+            for name, d, with_rho in (("parallax_d128", 128, True), ("softmax_d128", 128, False),
+                                      ("parallax_d64", 64, True)):
+                us, n_sets, how = time_point(B, L, d, with_rho, xs_cache)
+                row[name + "_us"] = round(us, 2)
+                row[name + "_GBs"] = round(4 * B * 8 * L * d / us / 1e3, 1)
+                row["timing_" + str(d)] = how
+            row["io_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d128_us"], 3)
+            row["compute_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d64_us"], 3)
+            points.append(row)
+            log(f"  sweep B={B} L={L}: parallax d128 {row['parallax_d128_us']} us, softmax {row['softmax_d128_us']} "
+                f"us, parallax d64 {row['parallax_d64_us']} us")
+    xs_cache.clear()
+    del flush, sink
+    torch.cuda.empty_cache()
+    io = [p["io_matched_speedup"] for p in points]
+    cm = [p["compute_matched_speedup"] for p in points]
+    big = [p for p in points if 4 * p["B"] * 8 * p["context"] * 128 >= (128 << 20)]
+    return {"heads": {"Hq": 16, "Hkv": 8}, "dtype": "bf16", "points": points, "skipped_for_time": skipped,
+            "seconds": round(time.time() - t_start, 1),
+            "io_matched_speedup_range": [min(io), max(io)] if io else None,
+            "compute_matched_speedup_range": [min(cm), max(cm)] if cm else None,
+            "bandwidth_bound_points": {"n": len(big),
+                                       "io_matched_geomean": _geomean([p["io_matched_speedup"] for p in big]),
+                                       "compute_matched_geomean": _geomean([p["compute_matched_speedup"]
+                                                                            for p in big])}}
 
-            def call():
-                plx.decode(x["q"], x["k"], x["v"], rho, out=out, workspace=ws)
 
-            us = timed(call, nbytes)
-            row[name + "_us"] = round(us, 2)
-            row[name + "_GBs"] = round(nbytes / us / 1e3, 1)
-            if us < 50:  # launch-bound sizes: also replayed from a graph
-                gus = graph_timed(call)
-                row[name + "_graph_us"] = round(gus, 2)
-                row[name + "_graph_GBs"] = round(nbytes / gus / 1e3, 1)
-            del x, out, ws
-        torch.cuda.empty_cache()
-        row["io_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d128_us"], 3)
-        row["compute_matched_speedup"] = round(row["softmax_d128_us"] / row["parallax_d64_us"], 3)
-        print(json.dumps(row), flush=True)
+def _geomean(xs):
+    return round(math.exp(sum(math.log(x) for x in xs) / len(xs)), 3) if xs else None
+
+
+def prefill_f32_leg(torch, plx, synth, steps=50):
+    """The fp32 causal prefill (B=1, Hq=Hkv=2, T=256, d=64): microseconds per
+    call, and every output row against the oracle."""
+    import oracle
+
+    w = synth.WORKLOADS["prefill_f32_b1_h2_t256_d64"]
+    x = synth.make_workload(w, "cuda")
+    out = torch.empty_like(x["q"])
+    secs, per = time_steps(lambda i: plx.prefill(x["q"], x["k"], x["v"], x["rho"], out=out), steps, 20, torch)
+    h = {n: x[n].double().cpu().numpy() for n in ("q", "k", "v", "rho")}
+    ref = oracle.prefill(h["q"], h["k"], h["v"], h["rho"], 1 / math.sqrt(w.d))
+    flops = 4 * 2 * w.d * w.B * w.Hq * w.T * (w.T + 1) // 2
+    return {"workload": w.name, "us_per_call": round(secs / steps * 1e6, 2),
+            "us_per_call_median": round(sorted(per)[len(per) // 2] * 1e3, 2), "steps": steps,
+            "tflops": round(flops / (secs / steps) / 1e12, 3), "bound": "launch latency (3.4e7 flop)",
+            "gpu_parity_vs_oracle": parity_errors(out.double().cpu().numpy(), ref)}
+
+
+def io_contract(torch, plx, synth, copy_mib: int):
+    """Decode workload calls for the counter runs that show the probe branch
+    adds no K/V traffic and no matrix instructions: a plain device copy of
+    copy_mib MiB (calibration), then three calls with rho and three with
+    rho = NULL on the same two input sets, in that order."""
+    dev = "cuda"
+    w = synth.WORKLOADS[DECODE_WL]
+    n = copy_mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    sets = [synth.make_decode(w.B, w.Hq, w.Hkv, w.L, w.d, w.dtype, dev, seed=s) for s in range(2)]
+    out = torch.empty_like(sets[0]["q"])
+    order = []
+    for with_rho in (True, False):
+        for i in range(3):
+            x = sets[i % 2]
+            plx.decode(x["q"], x["k"], x["v"], x["rho"] if with_rho else None, out=out)
+            order.append("rho" if with_rho else "rho=NULL")
+    torch.cuda.synchronize()
+    print(json.dumps({"io_contract": {"workload": w.name, "copy_bytes": n, "decode_calls_in_order": order,
+                                      "rho_bytes_per_call": 2 * w.B * w.Hq * w.d,
+                                      "kv_bytes_per_call": 2 * 2 * w.B * w.Hkv * w.L * w.d}}), flush=True)
 
 
 def other_decode_workloads(plx, synth, dev, torch):
@@ -393,7 +514,11 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--backward-warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
-                    help="decode sweep: Parallax vs softmax-only over batch x context (JSON lines)")
+                    help="run only the decode sweep (Parallax vs softmax-only over batch x context)")
+    ap.add_argument("--no-sweep", action="store_true", help="leave the decode sweep out of the default run")
+    ap.add_argument("--sweep-budget", type=float, default=60.0, help="seconds the decode sweep may take")
+    ap.add_argument("--io-contract", action="store_true",
+                    help="only the decode calls of the probe-traffic counter runs (with rho, then rho = NULL)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -414,8 +539,13 @@ def main():
     plx.load_library()
     dev = "cuda"
 
+    from transformer_attention_flash_amd import diag
+
+    if args.io_contract:
+        io_contract(torch, plx, synth, args.copy_probe_mib or 1024)
+        return
     if args.sweep:
-        run_sweep(args, torch, plx, synth)
+        print(json.dumps({"sweep": run_sweep(torch, plx, synth, diag, args.sweep_budget)}), flush=True)
         return
 
     if args.copy_probe_mib:
@@ -481,9 +611,13 @@ def main():
                           "tflops": round(flops / step_s / 1e12, 3)},
     }
 
+    result["build"] = build_info()
     if not args.no_cpu_baseline:
         log("decode CPU baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline_decode(sets[0], w, args.cpu_budget)
+        x0 = sets[0]
+        out0 = plx.decode(x0["q"], x0["k"], x0["v"], x0["rho"])
+        result["cpu_baseline"] = cpu_baseline_decode(x0, w, args.cpu_budget, gpu_out=out0)
+        del out0
     del sets
     torch.cuda.empty_cache()
     if not args.no_context:
@@ -546,7 +680,10 @@ def main():
             del lx, lout
         if not args.no_cpu_baseline:
             log("prefill CPU baseline (oracle)")
-            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(psets[0], pw, args.cpu_budget)
+            x0 = psets[0]
+            out0 = plx.prefill(x0["q"], x0["k"], x0["v"], x0["rho"])
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(x0, pw, args.cpu_budget, gpu_out=out0)
+            del out0
 
         # ---------------- fused q/k/v/probe projection of the same layer ----------------
         if not args.no_projection:
@@ -618,6 +755,13 @@ def main():
             if not args.no_cpu_baseline:
                 log("backward CPU baseline (oracle)")
                 result["prefill"]["backward"]["cpu_baseline"] = cpu_baseline_backward(x, dout, pw)
+
+    if not args.no_prefill:
+        log("fp32 prefill (B=1, Hq=Hkv=2, T=256, d=64)")
+        result["prefill_f32"] = prefill_f32_leg(torch, plx, synth)
+    if not args.no_sweep:
+        log(f"decode sweep (budget {args.sweep_budget:.0f} s)")
+        result["sweep"] = run_sweep(torch, plx, synth, diag, args.sweep_budget)
 
     if not args.no_device:
         log("device ceilings: streaming read, MFMA-only kernel")
