@@ -67,12 +67,17 @@ typedef enum {
     PLX_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size, bad scale */
     PLX_ERR_UNSUPPORTED = 2,         /* valid but not built: head dim, group size, dtype */
     PLX_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below the size query */
-    PLX_ERR_HIP = 4                  /* a launch failed (hipGetLastError) */
+    PLX_ERR_HIP = 4,                 /* a launch failed (hipGetLastError) */
+    /* Not a status: widens the type's range to every 32-bit value, so that
+     * any int a caller passes (say to parallax_status_string) is a valid
+     * value of the type in C++ as in C. */
+    PLX_STATUS_RANGE_ = 0x7fffffff
 } plx_status_t;
 
 typedef enum {
     PLX_DTYPE_F32 = 0,   /* IEEE float32 inputs and output */
-    PLX_DTYPE_BF16 = 1   /* bfloat16 inputs and output (round to nearest even) */
+    PLX_DTYPE_BF16 = 1,  /* bfloat16 inputs and output (round to nearest even) */
+    PLX_DTYPE_RANGE_ = 0x7fffffff  /* not a dtype: as PLX_STATUS_RANGE_ */
 } plx_dtype_t;
 
 /*
