@@ -12,15 +12,16 @@
 //
 // The kernel computes C^T = W x^T: output features along the MFMA rows (A
 // operand = weight rows), tokens along the columns (B operand = token rows),
-// both with the model dimension contiguous, so each lane ends up holding 4
-// consecutive head dimensions of one token and writes them with one 8-byte
-// store.  Block: 256 features x 256 tokens, 64-wide steps over d_model,
-// double-buffered in LDS (128 KB); 8 wavefronts, each 64 features x 128
-// tokens (4 x 8 tiles of v_mfma_f32_16x16x32_bf16), so every operand read
-// from LDS feeds 4 or 8 MFMAs.  The tiles move from global memory straight
-// into LDS (global_load_lds_dwordx4, no staging registers, no LDS store
-// instructions): 6% faster than loads staged through registers into padded
-// rows.
+// both with the model dimension contiguous.  Block: 256 features x 256
+// tokens; 8 wavefronts, each 64 features x 128 tokens (4 x 8 tiles of
+// v_mfma_f32_16x16x32_bf16), so every operand read from LDS feeds 4 or 8
+// MFMAs.  The model dimension is walked in 32-wide steps through five LDS
+// stages (5 x 32 KB): the tiles move from global memory straight into LDS
+// (global_load_lds_dwordx4, no staging registers, no LDS store instructions)
+// four steps ahead of their use, spread among the MFMAs, and the operands of
+// step st + 1 are read from LDS while the MFMAs of step st run.
+#include <type_traits>
+
 #include "plx_device.h"
 #include "plx_kernels.h"
 
@@ -30,33 +31,67 @@ namespace {
 
 constexpr int kPF = 256;        // features per block
 constexpr int kPT = 256;        // tokens per block
-constexpr int kPK = 64;         // model-dimension step
+constexpr int kPK = 32;         // model-dimension step
+constexpr int kPStages = 5;     // LDS stages (loads run kPStages - 1 steps ahead)
 constexpr int kPWaves = 8;
 constexpr int kXcdsP = 8;
 constexpr int kGroupT = 8;      // token blocks per L2 group
 
-// One 16-byte direct global-to-LDS load per lane (global_load_lds_dwordx4):
-// lane i writes bytes 16 i .. 16 i + 15 from the wavefront-uniform LDS
-// address `lds`.
-__device__ __forceinline__ void lds_load16(const void *g, void *lds) {
-    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// One 16-byte direct global-to-LDS load per lane (global_load_lds_dwordx4,
+// scalar-base form): lane i reads base + voff_bytes and writes LDS bytes
+// lds + 16 i .. lds + 16 i + 15; base and lds are wavefront-uniform (SGPRs,
+// lds through M0).  Written as assembly so that the compiler does not track
+// it: its own bookkeeping of such loads turns conservative with several LDS
+// stages in flight and makes every LDS read wait for all of them.  The kernel
+// orders its LDS reads after these loads itself (wait_stage), and leaves M0
+// to them alone.  An LDS DMA reads M0 one wait state after the scalar write
+// at the earliest, hence the s_nop.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff_bytes, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff_bytes),
+                 "s"(base)
+                 : "memory");
 }
-// An offset the optimizer cannot take apart (one move, outside the loop): the
-// compiler keeps its LDS alias information only for short address chains.
-__device__ __forceinline__ int opaque(int x) { return __builtin_amdgcn_mov_dpp(x, 0xE4, 0xF, 0xF, false); }
-// 16-byte chunk c of LDS row r (64 elements, 128 bytes, no padding) sits at
-// chunk c ^ swz(r).  Two rows share one 256-byte bank row, so the 16-byte bank
-// group of (r, c) is 8 (r & 1) + (c ^ swz(r)): for the 16 lanes that read
-// chunk c of 16 consecutive rows these are 16 different groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+// f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+// Sixteen bytes from LDS through an explicit LDS pointer.
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    return *(lds_u32x4 *)(p);
+}
+// All but this thread's N most recent direct loads have landed (they
+// complete in order), then a workgroup barrier that itself waits for nothing.
+template <int N>
+__device__ __forceinline__ void wait_stage() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 7 and lgkmcnt 15 (no wait).
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// 16-byte chunk c (0..3) of LDS row r (32 elements, 64 bytes, no padding)
+// sits at chunk c ^ swz(r).  Four rows share one 256-byte bank row, so the
+// 16-byte bank group of (r, c) is 4 (r & 3) + (c ^ swz(r)): for the 16 lanes
+// that read chunk c of 16 consecutive rows these are 16 different groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(ProjectionParams p) {
     using S = uint16_t;
-    // Two stages of the weight and token tiles, each buffer its own LDS array
-    // so that the compiler can tell the direct loads into one stage from the
-    // reads of the other.
-    __shared__ __attribute__((aligned(16))) S lds_w0[kPF * kPK], lds_w1[kPF * kPK];
-    __shared__ __attribute__((aligned(16))) S lds_x0[kPT * kPK], lds_x1[kPT * kPK];
+    // Five stages of the weight and token tiles (a stage: 256 weight rows,
+    // then 256 token rows, 32 elements each; 160 KB in all), carved from one
+    // array that afterwards holds the block's output tile.
+    constexpr int kStage = (kPF + kPT) * kPK;
+    __shared__ __attribute__((aligned(16))) S lds[kPStages * kStage];
+    static_assert(kPStages * kStage >= kPF * kPT, "the output tile reuses the stages");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -90,103 +125,161 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
     const S *xg = static_cast<const S *>(p.x);
 
     // Direct loads: slot n of this thread is LDS chunk (n * 8 + wave) * 64 + lane
-    // of the tile: row slot / 8, physical chunk slot % 8, holding global chunk
-    // (physical ^ swz(row)) of that row.
+    // of the tile: row slot / CPR, physical chunk slot % CPR, holding global
+    // chunk (physical ^ swz(row)) of that row.  Rows past the end of the
+    // weight or of the tokens re-read the last row (their results are not
+    // stored).  Byte offsets are taken from the block's first row, so they
+    // stay below 2^32 for any d_model up to 2^22.
     constexpr int CPR = kPK / 8;
     constexpr int NDW = kPF * CPR / (kPWaves * kWave);
     constexpr int NDX = kPT * CPR / (kPWaves * kWave);
-    int64_t wsrc[NDW], xsrc[NDX];
+    static_assert(NDW * kPWaves * kWave == kPF * CPR && NDX * kPWaves * kWave == kPT * CPR, "loader shape");
+    const S *wblk = wg + static_cast<int64_t>(f0) * K;
+    const S *xblk = xg + static_cast<int64_t>(t0) * K;
+    uint32_t wsrc[NDW], xsrc[NDX];
 #pragma unroll
     for (int n = 0; n < NDW; ++n) {
         const int s = (n * kPWaves + wave) * kWave + lane, r = s / CPR, c = (s % CPR) ^ swz(r);
-        wsrc[n] = static_cast<int64_t>(min(f0 + r, n_feat - 1)) * K + c * 8;
+        wsrc[n] = static_cast<uint32_t>((static_cast<int64_t>(min(f0 + r, n_feat - 1) - f0) * K + c * 8) * 2);
     }
 #pragma unroll
     for (int n = 0; n < NDX; ++n) {
         const int s = (n * kPWaves + wave) * kWave + lane, r = s / CPR, c = (s % CPR) ^ swz(r);
-        xsrc[n] = min(static_cast<int64_t>(t0 + r), M - 1) * K + c * 8;
+        xsrc[n] = static_cast<uint32_t>((min(static_cast<int64_t>(t0 + r), M - 1) - t0) * K * 2 + c * 16);
     }
-    auto dma = [&](int kk, S *lw, S *lx) {
-#pragma unroll
-        for (int n = 0; n < NDW; ++n) lds_load16(wg + wsrc[n] + kk, lw + (n * kPWaves + wave) * kWave * 8);
-#pragma unroll
-        for (int n = 0; n < NDX; ++n) lds_load16(xg + xsrc[n] + kk, lx + (n * kPWaves + wave) * kWave * 8);
+    const int n_steps = K / kPK;
+    const uint32_t wave_off = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave) * kWave * 16);
+    // Load n (0 .. NDW + NDX - 1) of step st (clamped to the last step: the
+    // loads past the end are harmless reloads that keep the number in flight
+    // constant) into the stage at lw.
+    auto dma_one = [&](int n, int st, const S *lw) __attribute__((always_inline)) {
+        const uint32_t kb = static_cast<uint32_t>(min(st, n_steps - 1) * kPK * 2);
+        if (n < NDW) dma16(wblk, wsrc[n] + kb, lds_address(lw) + wave_off + n * kPWaves * kWave * 16);
+        else dma16(xblk, xsrc[n - NDW] + kb, lds_address(lw + kPF * kPK) + wave_off + (n - NDW) * kPWaves * kWave * 16);
     };
+    constexpr int ND = NDW + NDX;
 
     constexpr int NI = 4, NJ = 8;
+    static_assert(ND <= NI, "one load per row of MFMAs");
     f32x4 acc[NI][NJ];
 #pragma unroll
     for (int a = 0; a < NI; ++a)
 #pragma unroll
         for (int b = 0; b < NJ; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Lane read offsets: row 16 i + col of the wavefront's part, chunk
-    // 4 ks + grp, swizzled by swz(row) = swz(col) (the part starts on a
-    // multiple of 16 rows).
-    int aoff[kPK / 32], boff[kPK / 32];
+    // Lane read offsets: row 16 i + col of the wavefront's part, chunk grp,
+    // swizzled by swz(row) = swz(col) (the part starts on a multiple of 16
+    // rows).
+    const int aoff = (16 * NI * wf + col) * kPK + (grp ^ swz(col)) * 8;
+    const int boff = (16 * NJ * wt + col) * kPK + (grp ^ swz(col)) * 8;
+    struct Ops {
+        Op8<BF16> a[NI], b[NJ];
+    };
+    auto read_ops = [&](Ops &o, int stage) __attribute__((always_inline)) {
+        const S *tw = lds + stage * kStage, *tx = tw + kPF * kPK;
 #pragma unroll
-    for (int ks = 0; ks < kPK / 32; ++ks) {
-        aoff[ks] = opaque((16 * NI * wf + col) * kPK + ((4 * ks + grp) ^ swz(col)) * 8);
-        boff[ks] = opaque((16 * NJ * wt + col) * kPK + ((4 * ks + grp) ^ swz(col)) * 8);
-    }
-    auto compute = [&](const S *tw, const S *tx) {
+        for (int i = 0; i < NI; ++i) o.a[i].w = lds_read16(tw + aoff + 16 * i * kPK);
 #pragma unroll
-        for (int ks = 0; ks < kPK / 32; ++ks) {
-            Op8<BF16> a[NI], b[NJ];
+        for (int j = 0; j < NJ; ++j) o.b[j].w = lds_read16(tx + boff + 16 * j * kPK);
+    };
+    // Step st: read the operands of step st + 1 (its stage landed before the
+    // last barrier), then the MFMAs of step st with the loads of step st + 4
+    // into the stage step st - 1 read spread among them -- the CU's memory
+    // pipeline takes these 1 KB requests at about 64 bytes a clock, so a
+    // wavefront issuing them back to back would stall -- then wait until only
+    // the loads of steps st + 3 and st + 4 are outstanding, i.e. step st + 2
+    // has landed for every thread, and meet at the barrier.
+    Ops ops0, ops1;
+    auto step = [&](int st, auto u_c, Ops &cur, Ops &nxt) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
+        if (st + 1 < n_steps) read_ops(nxt, (U + 1) % kPStages);
+        const S *lw = lds + ((U + kPStages - 1) % kPStages) * kStage;
+        static_for<0, NI>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int I = decltype(i_c)::value;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) a[i] = op8_load(tw + aoff[ks] + 16 * i * kPK);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) b[j] = op8_load(tx + boff[ks] + 16 * j * kPK);
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[i][j] = mma32(a[i], b[j], acc[i][j]);
-        }
+            for (int j = 0; j < NJ; ++j) acc[I][j] = mma32(cur.a[I], cur.b[j], acc[I][j]);
+            if constexpr (I < ND) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma_one(I, st + kPStages - 1, lw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        wait_stage<(kPStages - 3) * ND>();
     };
 
-    const int n_steps = K / kPK;
-    dma(0, lds_w0, lds_x0);
-    for (int s = 0; s < n_steps; s += 2) {
-        // Stage s is in buffer 0, stage s + 1 goes to buffer 1 (free: its last
-        // readers finished stage s - 1 before this barrier), and so on.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
-        __syncthreads();
-        if (s + 1 < n_steps) dma((s + 1) * kPK, lds_w1, lds_x1);
-        compute(lds_w0, lds_x0);
-        if (s + 1 < n_steps) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
-            if (s + 2 < n_steps) dma((s + 2) * kPK, lds_w0, lds_x0);
-            compute(lds_w1, lds_x1);
+    for (int st = 0; st < kPStages - 1; ++st)
+#pragma unroll
+        for (int n = 0; n < ND; ++n) dma_one(n, st, lds + st * kStage);
+    wait_stage<(kPStages - 3) * ND>();  // steps 0 and 1 have landed
+    read_ops(ops0, 0);
+    // Unrolled by ten so that every stage (st % 5) and operand set (st % 2)
+    // is named statically.
+    for (int st = 0; st < n_steps; st += 2 * kPStages) {
+        static_for<0, 2 * kPStages>([&](auto u) __attribute__((always_inline)) {
+            constexpr int U = decltype(u)::value;
+            if (st + U < n_steps) {
+                if constexpr (U % 2 == 0) step(st + U, std::integral_constant<int, U % kPStages>{}, ops0, ops1);
+                else step(st + U, std::integral_constant<int, U % kPStages>{}, ops1, ops0);
+            }
+        });
+    }
+    // The reloads past the end are still in flight: they land before the
+    // stages are overwritten with the output tile.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    // Epilogue through LDS: the stages are free once every wavefront has read
+    // its last one, and the 256 x 256 output tile (bf16, 128 KB) goes there
+    // as [token][feature] rows of 512 bytes; then each 16-byte chunk of a
+    // row -- 8 consecutive features, never across a head or a tensor, since
+    // d and the q/k/v/probe boundaries are multiples of 8 -- is stored with
+    // one 16-byte write, so the 16 chunks of a (token, head) row of d = 128
+    // go out as one 256-byte run.
+    // Row r keeps its 16-byte chunk c at c ^ (r % 16): the 16 tokens (rows
+    // r % 16 = col) of one accumulator write then spread over the banks, and
+    // a chunk's two 8-byte halves stay adjacent.
+    constexpr int ORS = kPF;  // output tile row: 256 features
+    {
+        // acc[i][j][e] is feature 128 wf + 16 i + 4 grp + e of token
+        // 128 wt + 16 j + col of the block.
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            S *row = lds + (16 * NJ * wt + 16 * j + col) * ORS;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int u = 4 * NI * wf + 4 * i + grp;  // 8-byte unit within the row
+                const float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                store4(row + 4 * (u ^ (2 * col)), y);
+            }
         }
     }
-
-    // acc[i][j][e] is feature f0 + 64 wf + 16 i + 4 grp + e of token
-    // t0 + 128 wt + 16 j + col.  Four consecutive features share a head.
+    __syncthreads();
+    // Thread tid stores chunk tid % 32 (features 8 (tid % 32) ..) of rows
+    // RPI it + tid / 32, it = 0 .. kPT / RPI - 1.
+    constexpr int RPI = kPWaves * kWave / 32;  // rows per pass
+    const int c16 = tid & 31;
+    const int f = f0 + 8 * c16;
+    if (f < n_feat) {
+        S *base;
+        int H, fl;
+        if (f < p.nq) {
+            base = static_cast<S *>(p.q); H = p.Hq; fl = f;
+        } else if (f < p.nq + p.nkv) {
+            base = static_cast<S *>(p.k); H = p.Hkv; fl = f - p.nq;
+        } else if (f < p.nq + 2 * p.nkv) {
+            base = static_cast<S *>(p.v); H = p.Hkv; fl = f - p.nq - p.nkv;
+        } else {
+            base = static_cast<S *>(p.rho); H = p.Hq; fl = f - p.nq - 2 * p.nkv;
+        }
+        const int h = fl / p.d, a = fl % p.d;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int64_t t = t0 + 16 * NJ * wt + 16 * j + col;
-        if (t >= M) continue;
-        const int64_t bb = t / p.T, tt = t % p.T;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            int f = f0 + 16 * NI * wf + 16 * i + 4 * grp;
-            if (f >= n_feat) continue;
-            void *base;
-            int H;
-            if (f < p.nq) {
-                base = p.q; H = p.Hq;
-            } else if (f < p.nq + p.nkv) {
-                base = p.k; H = p.Hkv; f -= p.nq;
-            } else if (f < p.nq + 2 * p.nkv) {
-                base = p.v; H = p.Hkv; f -= p.nq + p.nkv;
-            } else {
-                base = p.rho; H = p.Hq; f -= p.nq + 2 * p.nkv;
-            }
-            const int h = f / p.d, a = f % p.d;
-            S *dst = static_cast<S *>(base) + ((bb * H + h) * p.T + tt) * p.d + a;
-            float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            store4(dst, y);
+        for (int it = 0; it < kPT / RPI; ++it) {
+            const int r = RPI * it + (tid >> 5);
+            const int64_t t = t0 + r;
+            if (t >= M) break;
+            const u32x4 val = lds_read16(lds + r * ORS + 8 * (c16 ^ (r & 15)));
+            const int64_t bb = t / p.T, tt = t - bb * p.T;
+            *reinterpret_cast<u32x4 *>(base + ((bb * H + h) * p.T + tt) * p.d + a) = val;
         }
     }
 }
@@ -195,7 +288,8 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
 
 int projection_block_features() { return kPF; }
 int projection_block_tokens() { return kPT; }
-int projection_step() { return kPK; }
+// d_model granularity the entry point accepts (the kernel needs kPK).
+int projection_step() { return 2 * kPK; }
 
 hipError_t launch_projection(const ProjectionParams &p, hipStream_t stream) {
     hipLaunchKernelGGL(projection_kernel, dim3(static_cast<uint32_t>(p.n_fblk) * p.n_tblk), dim3(kPWaves * kWave),
