@@ -79,10 +79,12 @@ __device__ __forceinline__ void wait_stage() {
     asm volatile("" ::: "memory");
 }
 // 16-byte chunk c (0..3) of LDS row r (32 elements, 64 bytes, no padding)
-// sits at chunk c ^ swz(r).  Four rows share one 256-byte bank row, so the
-// 16-byte bank group of (r, c) is 4 (r & 3) + (c ^ swz(r)): for the 16 lanes
-// that read chunk c of 16 consecutive rows these are 16 different groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// sits at chunk c ^ swz(r).  An operand read has lane group grp read chunk
+// grp of 16 consecutive rows.  Measured on gfx950 (ds_read_b128, 8
+// wavefronts per CU): with swz(r) = (r >> 1) & 3 these reads take the 32
+// cycles per instruction that contiguous reads take; with (r >> 2) & 3 they
+// take 58, and unswizzled 64-byte rows 58 as well.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
 __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(ProjectionParams p) {
     using S = uint16_t;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kPWaves *kWave, 2) void projection_kernel(Projectio
 
     // Lane read offsets: row 16 i + col of the wavefront's part, chunk grp,
     // swizzled by swz(row) = swz(col) (the part starts on a multiple of 16
-    // rows).
+    // rows, and swz depends on row bits 1-2 only).
     const int aoff = (16 * NI * wf + col) * kPK + (grp ^ swz(col)) * 8;
     const int boff = (16 * NJ * wt + col) * kPK + (grp ^ swz(col)) * 8;
     struct Ops {
