@@ -115,6 +115,19 @@ def test_training_forward_outputs(rho):
         assert out_sa is None
 
 
+def test_backward_deterministic():
+    """No atomics anywhere in the training forward or the backward: two runs on
+    the same inputs (several key blocks, query steps and a ragged tail) give
+    bitwise-equal statistics and gradients."""
+    say("backward determinism B=2 Hq=4 Hkv=2 T=257 d=128 rho")
+    x = _inputs(2, 4, 2, 257, 128, True, seed=5)
+    scale = 1.0 / math.sqrt(128)
+    fw1, g1 = _run(x, scale)
+    fw2, g2 = _run(x, scale)
+    for name, a, b in zip(("out", "out_sa", "lse", "rbar", "dq", "dk", "dv", "drho"), (*fw1, *g1), (*fw2, *g2)):
+        assert torch.equal(a, b), f"{name} differs between two identical runs"
+
+
 def test_autograd_wrapper_matches_entry_points():
     plx = _plx()
     x = _inputs(1, 4, 2, 96, 64, True, seed=3)

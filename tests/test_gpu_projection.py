@@ -50,6 +50,20 @@ def test_projection_matches_oracle(B, T, dm, Hq, Hkv, d):
         _check(got, ref, name)
 
 
+def test_projection_deterministic():
+    """Each output element is one block's fp32 sum in a fixed order: two calls
+    (several feature and token blocks, a ragged token tail) are bitwise equal."""
+    import transformer_attention_flash_amd as plx
+    from transformer_attention_flash_amd import synth
+    say("projection determinism B=2 T=600 d_model=256 Hq=4 Hkv=2 d=128")
+    x, w = synth.make_projection(2, 600, 256, 4, 2, 128, torch.bfloat16, "cuda", seed=3)
+    a = plx.qkvr_projection(x, w, 4, 2, 128)
+    b = plx.qkvr_projection(x, w, 4, 2, 128)
+    torch.cuda.synchronize()
+    for name, u, v in zip(("q", "k", "v", "rho"), a, b):
+        assert torch.equal(u, v), f"{name} differs between two identical calls"
+
+
 def test_projection_full_size_sampled_tokens():
     """The prefill workload's projection (B=8, T=4096, d_model=2048, Hq=16,
     Hkv=8, d=128): 96 sampled tokens against the oracle, every output
