@@ -85,8 +85,14 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
     constexpr bool FULL = KCH % NTHR == 0;
     static_assert(16 % G == 0, "group size must divide the wavefront's 16 rows");
 
-    __shared__ __attribute__((aligned(16))) S lds_k[2][KT * RS];
-    __shared__ __attribute__((aligned(16))) S lds_v[2][KT * RS];
+    // TPB tiles per barrier, 2 TPB buffers: a barrier opens tiles j .. j + TPB - 1,
+    // and tiles j + TPB .. j + 2 TPB - 1 are stored meanwhile into the buffers
+    // of tiles j - TPB .. j - 1, whose readers all finished before that
+    // barrier (as in the forward kernel).
+    constexpr int TPB = 2;  // measured ~2% faster for this kernel than one tile per barrier
+    constexpr int NBUF = 2 * TPB;
+    __shared__ __attribute__((aligned(16))) S lds_k[NBUF][KT * RS];
+    __shared__ __attribute__((aligned(16))) S lds_v[NBUF][KT * RS];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -201,11 +207,15 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
 
     load_tile(0);
     store_tile(0);
+    if (TPB > 1 && n_tiles > 1) {
+        load_tile(1);
+        store_tile(1);
+    }
     for (int j = 0; j < n_tiles; ++j) {
-        const int buf = j & 1;
-        __syncthreads();
-        const bool more = j + 1 < n_tiles;
-        if (more) load_tile(j + 1);
+        const int buf = j & (NBUF - 1);
+        if (j % TPB == 0) __syncthreads();
+        const bool more = j + TPB < n_tiles;
+        if (more) load_tile(j + TPB);
         const int key0 = j * KT;
         if (key0 <= wpos_last) {
             const S *kt = lds_k[buf];
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (more) store_tile(buf ^ 1);
+        if (more) store_tile((j + TPB) & (NBUF - 1));
     }
 
     if (pos < T_len) {
