@@ -175,7 +175,7 @@ size_t parallax_bwd_prefill_workspace_size(int32_t B, int32_t Hq, int32_t T);
  * that does not match rho's, misaligned pointers, non-positive sizes, a bad
  * scale, or an output overlapping an input, another output or the
  * workspace; PLX_ERR_WORKSPACE_TOO_SMALL; PLX_ERR_UNSUPPORTED for
- * dtype != PLX_DTYPE_BF16, other d or group sizes.
+ * dtype != PLX_DTYPE_BF16, other d or group sizes, or T * (Hq / Hkv) >= 2^31.
  */
 plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v,
                                   const void *rho, const void *out,

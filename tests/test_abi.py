@@ -117,6 +117,7 @@ def backward(lib, q=P[0], k=P[1], v=P[2], rho=P[3], out=P[4], out_sa=P[5], lse=P
     (dict(rho=None), INVALID),                 # drho/out_sa/rbar given without rho
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(scale=0.0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
     (dict(dtype=F32), UNSUP), (dict(d=32), UNSUP), (dict(Hq=48, Hkv=2), UNSUP),
+    (dict(Hq=8, Hkv=1, T=1 << 28, ws_bytes=1 << 40), UNSUP),  # T * G = 2^31 rows per KV group
     (dict(ws_bytes=1023), WS),                 # needs 1 * 4 * 16 * 16 = 1024 bytes
     (dict(dq=P[0]), INVALID),                  # dq aliases q
     (dict(dv=P[10] + 32), INVALID),            # dv overlaps dk

@@ -284,6 +284,8 @@ plx_status_t parallax_bwd_prefill(const void *q, const void *k, const void *v, c
     const size_t need = parallax_bwd_prefill_workspace_size(B, Hq, T);
     if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
     const int G = Hq / Hkv;
+    // The kernels index the rows of a KV group (position x G + head) in 32 bits.
+    if (static_cast<int64_t>(T) * G >= (int64_t{1} << 31)) return PLX_ERR_UNSUPPORTED;
     const int bq = plx::backward_q_block_positions(G);
     const int kb = plx::backward_k_block_keys();
     const int64_t n_qblk = (static_cast<int64_t>(T) + bq - 1) / bq;

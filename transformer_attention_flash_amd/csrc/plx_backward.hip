@@ -347,15 +347,16 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
     const int k0 = kblk * KB;
     const int kw0 = k0 + 16 * wave;         // this wavefront's first key
     const int key = kw0 + col;              // this lane's key
-    const int64_t rows_total = static_cast<int64_t>(T_len) * G;
-    const int64_t r0 = static_cast<int64_t>(k0) * G;  // first row that can see key k0
-    const int n_steps = static_cast<int>((rows_total - r0 + QR - 1) / QR);
+    // Row indices of the KV group are 32-bit: the entry point rejects T G >= 2^31.
+    const int rows_total = T_len * G;
+    const int r0 = k0 * G;  // first row that can see key k0
+    const int n_steps = (rows_total - r0 + QR - 1) / QR;
     // Steps walk the rows from the last one backwards on a grid common to all
     // key blocks (step s covers rows rows_total - (s+1) QR .. rows_total - s QR - 1),
     // so the concurrently running key blocks of one KV head read the same
     // tile at about the same time and it is fetched into L2 once.  Rows
     // before r0 in the last step (negative indices included) are masked.
-    auto step_row0 = [&](int step) { return rows_total - static_cast<int64_t>(step + 1) * QR; };
+    auto step_row0 = [&](int step) { return rows_total - (step + 1) * QR; };
 
     const int64_t kv_base = (static_cast<int64_t>(b) * p.Hkv + g) * T_len * static_cast<int64_t>(D);
     // The wavefront's keys as the B operand (column = key): K[key][dims].
@@ -374,25 +375,33 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
     // Row tile loader: thread tid moves chunks tid, tid + NTHR, ... of each tensor.
     Op8<BF16> stg[NQC][NTEN];
     float4 stst = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto row_ptr_off = [&](int64_t r) {  // element offset of row r of the KV group in a [B, Hq, T, D] tensor
-        const int64_t rr = min(max(r, int64_t{0}), rows_total - 1);
-        const int64_t pp = rr / G;
-        const int hh = g * G + static_cast<int>(rr % G);
-        return ((static_cast<int64_t>(b) * p.Hq + hh) * T_len + pp);
-    };
+    // Loader rows: chunk n of this thread is row lrow of the step, 8-element
+    // column chunk cc.  A step's first row rs0 is a multiple of G (rows_total
+    // = T G and QR are), so row rs0 + lrow is position rs0 / G + lrow / G of
+    // query head g G + lrow % G: the head is fixed, and only the position
+    // moves, by QR / G per step.  Only the last step reaches below position 0
+    // (rows that are masked); their loads are clamped to position 0.
+    static_assert(QR % 8 == 0 && QFULL, "loader rows");
+    int64_t lbase[NQC];  // element offset of (head, position 0, column chunk)
+    int lpos[NQC];       // lrow / G
+#pragma unroll
+    for (int n = 0; n < NQC; ++n) {
+        const int c = tid + n * NTHR, lrow = c / (D / 8), cc = c % (D / 8);
+        lbase[n] = (static_cast<int64_t>(b) * p.Hq + g * G + lrow % G) * T_len * static_cast<int64_t>(D) + cc * 8;
+        lpos[n] = lrow / G;
+    }
+    const int64_t sbase = (static_cast<int64_t>(b) * p.Hq + g * G + tid % G) * T_len;  // row statistics, tid < QR
+    const int spos = tid / G;
     auto load_step = [&](int step) {
-        const int64_t rs0 = step_row0(step);
+        const int pos0 = step_row0(step) / G;  // exact: step_row0 is a multiple of G
 #pragma unroll
         for (int n = 0; n < NQC; ++n) {
-            const int c = tid + n * NTHR;
-            if (QFULL || c < QCH) {
-                const int64_t off = row_ptr_off(rs0 + c / (D / 8)) * D + (c % (D / 8)) * 8;
-                stg[n][0] = op8_load(static_cast<const S *>(p.q) + off);
-                stg[n][1] = op8_load(static_cast<const S *>(p.dout) + off);
-                if constexpr (HAS_RHO) stg[n][2] = op8_load(static_cast<const S *>(p.rho) + off);
-            }
+            const int64_t off = lbase[n] + static_cast<int64_t>(max(pos0 + lpos[n], 0)) * D;
+            stg[n][0] = op8_load(static_cast<const S *>(p.q) + off);
+            stg[n][1] = op8_load(static_cast<const S *>(p.dout) + off);
+            if constexpr (HAS_RHO) stg[n][2] = op8_load(static_cast<const S *>(p.rho) + off);
         }
-        if (tid < QR) stst = p.rowst[row_ptr_off(rs0 + tid)];
+        if (tid < QR) stst = p.rowst[sbase + max(pos0 + spos, 0)];
     };
     auto store_step = [&](int buf) {
 #pragma unroll
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
         __syncthreads();
         const bool more = step + 1 < n_steps;
         if (more) load_step(step + 1);
-        const int64_t rs0 = step_row0(step);
+        const int rs0 = step_row0(step);
         // Rows of this step reach position (rs0 + QR - 1) / G; the wavefront's
         // keys start at kw0.  Skip (wavefront-uniformly) when no row can see them.
         if ((rs0 + QR - 1) / G >= kw0 && kw0 < T_len) {
@@ -456,9 +465,12 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
             for (int e = 0; e < 4 * NQB; ++e) {
                 const int qb = e >> 2, i = e & 3;
                 const int lr = 16 * qb + 4 * grp + i;  // row within the step
-                const int64_t r = rs0 + lr;
+                const int r = rs0 + lr;
                 const float4 st = lds_st[buf][lr];     // (lse, rbar, G, D)
-                const bool valid = r >= r0 && key <= static_cast<int>(r / G) && key < T_len;
+                // Rows reach position T - 1 at most, so keys past the sequence
+                // fail the causal test too; negative rows (the last step) fail
+                // the first.
+                const bool valid = r >= r0 && key <= static_cast<int>(static_cast<unsigned>(r) / G);
                 float pr = fast_exp2(fmaf(sacc[qb][i], p.scale_log2, -st.x));
                 if (!valid) pr = 0.f;
                 const float gv = gacc[qb][i];
