@@ -22,7 +22,7 @@
 //   bwd_dq_kernel       a workgroup of 8 wavefronts owns 128 query rows (as
 //                       the forward) and streams K/V tiles; dq and drho come
 //                       out of one transposed read of the K tile.  It also
-//                       forms each row's (lse, rbar, G, D) and keeps them in
+//                       forms each row's (lse, 1 + rbar, G, -D) and keeps them in
 //                       the workspace for the next kernel.
 //   bwd_dkdv_kernel     a workgroup of 8 wavefronts owns 128 keys (16 per
 //                       wavefront, held in registers) and streams 64-row
@@ -161,7 +161,9 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
     const float rbar = HAS_RHO ? p.rbar[row] : 0.f;
     const float Gi = HAS_RHO ? dot_sa : dot_o;
     const float Di = HAS_RHO ? dot_o + rbar * Gi : dot_o;
-    if (grp == 0 && pos < T_len) p.rowst[row] = make_float4(lse, rbar, Gi, Di);
+    const float one_rbar = 1.f + rbar, neg_D = -Di;
+    // Kept as (lse, 1 + rbar, G, -D): the forms the elementwise terms use.
+    if (grp == 0 && pos < T_len) p.rowst[row] = make_float4(lse, 1.f + rbar, Gi, -Di);
 
     int g_off[NKC], l_off[NKC];
 #pragma unroll
@@ -243,19 +245,26 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
 
             const bool diag = key0 + KT - 1 > wpos0;
             const int rel = pos - key0 - 4 * grp;  // key > pos <=> offset > rel
+            // dS / scale (the scale multiplies dq once, in the epilogue) and dR.
             float ds[NKB * 4], dr[HAS_RHO ? NKB * 4 : 1];
+            // Causal mask, on the tiles that cross the diagonal only (wave-uniform):
+            // a masked score becomes -inf, so its p is 0 (the scale is positive).
+            if (diag) {
+#pragma unroll
+                for (int e = 0; e < NKB * 4; ++e)
+                    if (16 * (e >> 2) + (e & 3) > rel) sacc[e >> 2][e & 3] = -INFINITY;
+            }
 #pragma unroll
             for (int e = 0; e < NKB * 4; ++e) {
                 const int kb = e >> 2, i = e & 3;
-                float pr = fast_exp2(fmaf(sacc[kb][i], p.scale_log2, -lse));
-                if (diag && 16 * kb + i > rel) pr = 0.f;
+                const float pr = fast_exp2(fmaf(sacc[kb][i], p.scale_log2, -lse));
                 const float gv = gacc[kb][i];
                 if constexpr (HAS_RHO) {
                     const float rv = racc[kb][i];
-                    ds[e] = p.scale * pr * (gv * (1.f - rv + rbar) + Gi * rv - Di);
+                    ds[e] = pr * fmaf(gv, one_rbar - rv, fmaf(Gi, rv, neg_D));
                     dr[e] = pr * (Gi - gv);
                 } else {
-                    ds[e] = p.scale * pr * (gv - Di);
+                    ds[e] = pr * (gv + neg_D);
                 }
             }
             Op8<BF16> dsop[NU], drop[HAS_RHO ? NU : 1];
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dq_kernel(BackwardPar
         for (int t = 0; t < DT; ++t) {
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = dqacc[t][i];
+            for (int i = 0; i < 4; ++i) y[i] = p.scale * dqacc[t][i];
             store4(dq + 16 * t + 4 * grp, y);
             if constexpr (HAS_RHO) {
 #pragma unroll
@@ -461,28 +470,35 @@ __global__ __launch_bounds__(kBwdWaves *kWave, 2) void bwd_dkdv_kernel(BackwardP
             __builtin_amdgcn_s_setprio(0);
 
             float w[4 * NQB], ds[4 * NQB], dr[HAS_RHO ? 4 * NQB : 1];
+            // Causal mask, only on steps whose first row comes before the
+            // wavefront's last key or before r0 (wavefront-uniform): a masked
+            // score becomes -inf, so its p is 0 (the scale is positive).  Rows
+            // reach position T - 1 at most, so keys past the sequence fail the
+            // causal test too; negative rows (the last step) fail the first.
+            if (rs0 < r0 || rs0 / G < kw0 + 15) {
+#pragma unroll
+                for (int e = 0; e < 4 * NQB; ++e) {
+                    const int r = rs0 + 16 * (e >> 2) + 4 * grp + (e & 3);
+                    if (!(r >= r0 && key <= static_cast<int>(static_cast<unsigned>(r) / G)))
+                        sacc[e >> 2][e & 3] = -INFINITY;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4 * NQB; ++e) {
                 const int qb = e >> 2, i = e & 3;
                 const int lr = 16 * qb + 4 * grp + i;  // row within the step
-                const int r = rs0 + lr;
-                const float4 st = lds_st[buf][lr];     // (lse, rbar, G, D)
-                // Rows reach position T - 1 at most, so keys past the sequence
-                // fail the causal test too; negative rows (the last step) fail
-                // the first.
-                const bool valid = r >= r0 && key <= static_cast<int>(static_cast<unsigned>(r) / G);
-                float pr = fast_exp2(fmaf(sacc[qb][i], p.scale_log2, -st.x));
-                if (!valid) pr = 0.f;
+                const float4 st = lds_st[buf][lr];     // (lse, 1 + rbar, G, -D)
+                const float pr = fast_exp2(fmaf(sacc[qb][i], p.scale_log2, -st.x));
                 const float gv = gacc[qb][i];
                 if constexpr (HAS_RHO) {
                     const float rv = racc[qb][i];
-                    const float f = 1.f - rv + st.y;
+                    const float f = st.y - rv;
                     w[e] = pr * f;
-                    ds[e] = p.scale * pr * (gv * f + st.z * rv - st.w);
+                    ds[e] = (p.scale * pr) * fmaf(gv, f, fmaf(st.z, rv, st.w));
                     dr[e] = pr * (st.z - gv);
                 } else {
                     w[e] = pr;
-                    ds[e] = p.scale * pr * (gv - st.w);
+                    ds[e] = (p.scale * pr) * (gv + st.w);
                 }
             }
             Op8<BF16> wop[NUQ], dsop[NUQ], drop[HAS_RHO ? NUQ : 1];

@@ -44,7 +44,7 @@ struct BackwardParams {
     const float *lse, *rbar;       // forward row statistics
     const void *dout;              // [B, Hq, T, D] upstream gradient
     void *dq, *dk, *dv, *drho;     // gradients, shaped like q, k, v, rho
-    float4 *rowst;                 // workspace [B, Hq, T]: (lse, rbar, G, Dsum)
+    float4 *rowst;                 // workspace [B, Hq, T]: (lse, 1 + rbar, G, -Dsum)
     int32_t B, Hq, Hkv, T;
     int32_t n_qblk;                // dq kernel: query blocks per (b, kv head)
     int32_t n_kblk;                // dk/dv kernel: key blocks per (b, kv head)
