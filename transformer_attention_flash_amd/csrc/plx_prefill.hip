@@ -127,9 +127,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     // bf16 with a probe runs a persistent grid (one workgroup per CU, which
     // is all the registers allow): a workgroup's output stores then drain
     // while its next item starts, instead of holding the CU until they are
-    // acknowledged (measured 2-3% faster).  The softmax-only kernel fits two
-    // workgroups per CU, which hide each other's ends, and keeps one item
-    // per workgroup.
+    // acknowledged, and the next item's q / rho loads are issued during the
+    // current item's last tile (measured 3-4% faster together).  The
+    // softmax-only kernel fits two workgroups per CU, which hide each other's
+    // ends, and keeps one item per workgroup.
     constexpr bool PERSIST = VNAT && HAS_RHO;
     constexpr int NBUF = 2 * TPB;
     __shared__ __attribute__((aligned(16))) S lds_k[NBUF][KT * KRS];
@@ -137,9 +138,57 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
 
     const int n_units = p.B * p.Hkv;
 
+    // Item id -> (query block, unit).  Workgroups are dealt to the 8 XCDs
+    // round-robin by id, and each XCD has its own 4 MB L2.  When the
+    // (b, kv head) units divide evenly, XCD x runs units x, x + 8, ... one
+    // after another, each with its query blocks longest first: the CUs of an
+    // XCD then stream the same unit's K/V (2 MB at T = 4096, d = 128)
+    // together, so it is fetched into L2 about once instead of once per
+    // query block.
+    auto item_of = [&](int id, int &qb, int &unit) __attribute__((always_inline)) {
+        if (n_units % kXcds == 0) {
+            const int xcd = id % kXcds, slot = id / kXcds;
+            qb = p.n_qblk - 1 - slot % p.n_qblk;
+            unit = xcd + kXcds * (slot / p.n_qblk);
+        } else {  // longest query blocks first
+            qb = p.n_qblk - 1 - id / n_units;
+            unit = id % n_units;
+        }
+    };
+    // The q and rho operands of this lane's rows in item id: column tile nb,
+    // column col -> row r = 16*nb + col of the wavefront, position
+    // wpos0 + r / G, query head g*G + r % G.
+    auto load_rows = [&](int id, int wave, int col, int grp, Op8<T> (&q)[NB][KS],
+                         Op8<T> (&rr)[NB][HAS_RHO ? KS : 1]) __attribute__((always_inline)) {
+        int qb, unit;
+        item_of(id, qb, unit);
+        const int b = unit / p.Hkv, g = unit % p.Hkv;
+        const int wpos0 = qb * BQ + wave * PW;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int r = 16 * nb + col;
+            const int head = g * G + r % G;
+            const int64_t off = ((static_cast<int64_t>(b) * p.Hq + head) * p.T + min(wpos0 + r / G, p.T - 1)) * D;
+            const S *qrow = static_cast<const S *>(p.q) + off;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) q[nb][s] = op8_load(qrow + 32 * s + 8 * grp);
+            if constexpr (HAS_RHO) {
+                const S *rrow = static_cast<const S *>(p.rho) + off;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) rr[nb][s] = op8_load(rrow + 32 * s + 8 * grp);
+            }
+        }
+    };
+    // Persistent grid: the next item's q and rho operands, requested during
+    // the current item's last tile (after its last score products, when the
+    // current operands are dead), so that their memory latency runs under
+    // that tile's softmax and value products and the epilogue.
+    Op8<T> nq[NB][KS];
+    Op8<T> nr[NB][HAS_RHO ? KS : 1];
+
     // One work item: item `id` of the grid order below, from its first K/V
-    // tile to its output rows.
-    auto run_item = [&](int id) __attribute__((always_inline)) {
+    // tile to its output rows; `next` is the item to request operands for.
+    auto run_item = [&](int id, int next) __attribute__((always_inline)) {
         int tid = threadIdx.x;
         // In the persistent loop nothing derived from the lane index is hoisted
         // out of the item loop (the hoisted values would stay live across the
@@ -150,21 +199,8 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
         const int col = lane & 15;
         const int grp = lane >> 4;
 
-        // Workgroups are dealt to the 8 XCDs round-robin by id, and each XCD has
-        // its own 4 MB L2.  When the (b, kv head) units divide evenly, XCD x runs
-        // units x, x + 8, ... one after another, each with its query blocks
-        // longest first: the CUs of an XCD then stream the same unit's K/V
-        // (2 MB at T = 4096, d = 128) together, so it is fetched into L2 about
-        // once instead of once per query block.
         int qb, unit;
-        if (n_units % kXcds == 0) {
-            const int xcd = id % kXcds, slot = id / kXcds;
-            qb = p.n_qblk - 1 - slot % p.n_qblk;
-            unit = xcd + kXcds * (slot / p.n_qblk);
-        } else {  // longest query blocks first
-            qb = p.n_qblk - 1 - id / n_units;
-            unit = id % n_units;
-        }
+        item_of(id, qb, unit);
         const int b = unit / p.Hkv;
         const int g = unit % p.Hkv;
         const int T_len = p.T;
@@ -191,14 +227,17 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
             pos[nb] = wpos0 + r / G;
             const int head = g * G + r % G;
             qoff[nb] = ((static_cast<int64_t>(b) * p.Hq + head) * T_len + min(pos[nb], T_len - 1)) * D;
-            const S *qrow = static_cast<const S *>(p.q) + qoff[nb];
+        }
+        if constexpr (PERSIST) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) qop[nb][s] = op8_load(qrow + 32 * s + 8 * grp);
-            if constexpr (HAS_RHO) {
-                const S *rrow = static_cast<const S *>(p.rho) + qoff[nb];
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int s = 0; s < KS; ++s) rop[nb][s] = op8_load(rrow + 32 * s + 8 * grp);
-            }
+                for (int s = 0; s < KS; ++s) {
+                    qop[nb][s] = nq[nb][s];
+                    if constexpr (HAS_RHO) rop[nb][s] = nr[nb][s];
+                }
+        } else {
+            load_rows(id, wave, col, grp, qop, rop);
         }
 
         // Loader registers for one tile.
@@ -302,7 +341,9 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
             store_tile(1);
         }
 
-        for (int j = 0; j < n_tiles; ++j) {
+        // One key tile; on the last tile of a persistent item (`last`) the
+        // next item's q and rho operands are requested.
+        auto tile_step = [&](const int j, auto last) __attribute__((always_inline)) {
             const int buf = j & (NBUF - 1);
             if (j % TPB == 0) __syncthreads();  // tiles j .. j + TPB - 1 are in LDS; the other buffers are free
             const bool more = j + TPB < n_tiles;
@@ -375,6 +416,10 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                     for (int u = 0; u < NU; ++u)
 #pragma unroll
                         for (int t = 0; t < DT; ++t) vop_all[u][t] = load_vop(u, t);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (decltype(last)::value) {
+                    load_rows(next, wave, col, grp, nq, nr);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 Op8<T> pop[NB][NU];
@@ -451,10 +496,18 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                         }
                     }
                 }
+            } else if constexpr (decltype(last)::value) {
+                load_rows(next, wave, col, grp, nq, nr);
             }
 
             __builtin_amdgcn_s_setprio(0);
             if (more) store_tile((j + TPB) & (NBUF - 1));
+        };
+        if constexpr (PERSIST) {
+            for (int j = 0; j < n_tiles - 1; ++j) tile_step(j, std::false_type{});
+            tile_step(n_tiles - 1, std::true_type{});
+        } else {
+            for (int j = 0; j < n_tiles; ++j) tile_step(j, std::false_type{});
         }
 
         // Epilogue: acc[nb][t][i] is head-dim 16*t + 4*grp + i of this lane's row.
@@ -550,15 +603,32 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
         const int n_items = n_units * p.n_qblk;
         const bool persist = static_cast<int>(gridDim.x) < n_items;
         const int xcd = blockIdx.x % kXcds, c = blockIdx.x / kXcds, ncu = gridDim.x / kXcds;
-        for (int r = 0;; ++r) {
-            const int id = persist ? xcd + kXcds * (r * ncu + ((r & 1) ? ncu - 1 - c : c))
-                                   : (r == 0 ? static_cast<int>(blockIdx.x) : n_items);
-            if (id >= n_items) break;  // later rounds only hold larger slots
-            run_item(id);
-            __syncthreads();  // the next item's first tiles overwrite LDS buffers 0 and 1
+        auto item_at = [&](int r) {
+            return persist ? xcd + kXcds * (r * ncu + ((r & 1) ? ncu - 1 - c : c))
+                           : (r == 0 ? static_cast<int>(blockIdx.x) : n_items);
+        };
+        const int lane0 = threadIdx.x & (kWave - 1);
+        int id = item_at(0);
+        if (id < n_items) load_rows(id, threadIdx.x / kWave, lane0 & 15, lane0 >> 4, nq, nr);
+        for (int r = 0; id < n_items; ++r) {  // later rounds only hold larger slots
+            const int next = item_at(r + 1);
+            // With no next item the last tile requests this item's rows again
+            // (always a valid address; unused).
+            run_item(id, next < n_items ? next : id);
+            // The next item's first tiles overwrite LDS buffers 0 and 1, so all
+            // waves meet here.  Every LDS read of this item has completed (its
+            // data fed the value products before the epilogue), so the barrier
+            // needs no wait: this item's output stores and the next item's
+            // q / rho loads stay in flight (__syncthreads() would wait for
+            // them).  The empty asm statements keep the compiler from moving
+            // memory accesses across the barrier.
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            id = next;
         }
     } else {
-        run_item(blockIdx.x);
+        run_item(blockIdx.x, blockIdx.x);
     }
 }
 
