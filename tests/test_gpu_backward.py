@@ -171,6 +171,37 @@ def test_backward_full_size_sampled_group_and_invariants():
     assert rel_k <= 1e-2
 
 
+def test_backward_persistent_grid_ragged():
+    """B=4, Hq=16, Hkv=8, T=1100, d=128 with a probe: 576 dq items and 288
+    dk/dv items, more than one workgroup per CU, so both kernels run their
+    persistent loops, and T is ragged against both the 64-row and the
+    128-key blocks.  The dk/dv items of sequence 3 are the ones the odd
+    persistent round takes (key blocks 5-8, walking their rows forwards);
+    its KV head 5 and sequence 0's KV head 2 (even rounds, backward walks)
+    against the oracle, and the two gradient invariants over every group."""
+    from oracle import grad as ograd
+    B, Hq, Hkv, T, d = 4, 16, 8, 1100, 128
+    say(f"persistent-grid backward B={B} Hq={Hq} Hkv={Hkv} T={T} d={d}")
+    x = _inputs(B, Hq, Hkv, T, d, True, seed=5)
+    scale = 1.0 / math.sqrt(d)
+    _, (dq, dk, dv, drho) = _run(x, scale)
+    G = Hq // Hkv
+    for b, g in ((3, 5), (0, 2)):
+        hs = slice(g * G, (g + 1) * G)
+        h = {n: host64(x[n][b:b + 1, hs] if n in ("q", "rho", "dout") else x[n][b:b + 1, g:g + 1]) for n in x}
+        ref = ograd.grad_expanded(h["q"], h["k"], h["v"], h["rho"], h["dout"], scale, groups=[(0, 0)])[(0, 0)]
+        _check_grad(dq[b, hs], ref[0], f"dq (b={b}, kv head {g})")
+        _check_grad(dk[b, g], ref[1], f"dk (b={b}, kv head {g})")
+        _check_grad(dv[b, g], ref[2], f"dv (b={b}, kv head {g})")
+        _check_grad(drho[b, hs], ref[3], f"drho (b={b}, kv head {g})")
+    dsum = x["dout"].double().reshape(B, Hkv, G, T, d).sum(dim=(2, 3))
+    rel_v = float((dv.double().sum(dim=2) - dsum).norm() / dsum.norm())
+    rel_k = float(dk.double().sum(dim=2).norm() / dk.double().abs().sum(dim=2).norm())
+    say(f"  sum_j dv_j vs sum dO: rel {rel_v:.3e}; |sum_j dk_j| / sum_j |dk_j|: {rel_k:.3e}")
+    assert rel_v <= 1e-2
+    assert rel_k <= 1e-2
+
+
 def test_backward_beyond_2_31_elements():
     """B=1100, Hq=16, Hkv=8, T=1024, d=128 with a probe: q, rho, dO, o, o^SA,
     dq and drho hold 2.3e9 elements each, so the last sequences sit past

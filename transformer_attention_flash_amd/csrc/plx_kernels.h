@@ -62,6 +62,10 @@ struct ProjectionParams {
     int32_t n_fblk, n_tblk;        // feature and token blocks
 };
 
+// Compute units of the current device (cached per device; 0 if the query
+// fails).  The persistent kernels launch one workgroup per CU.
+int device_cus();
+
 // Both return the first launch error (hipSuccess when everything queued).
 hipError_t launch_decode(const DecodeParams &p, bool bf16, int D, int G, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, bool bf16, int D, int G, bool has_rho,

@@ -632,9 +632,6 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
     }
 }
 
-namespace {
-
-// Compute units of the current device (cached per device).
 int device_cus() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cus[kMaxDevices];
@@ -647,6 +644,8 @@ int device_cus() {
     }
     return n;
 }
+
+namespace {
 
 template <class T, int D, int G, bool R>
 hipError_t launch_prefill_r(const PrefillParams &p, hipStream_t stream) {
