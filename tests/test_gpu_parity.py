@@ -233,6 +233,34 @@ def test_decode_sharp_scores():
         assert_within_bound(host64(out), ref, bound, f"decode sharp ks={ks}")
 
 
+# More items than CUs: the bf16 kernel with a probe then runs its persistent
+# loop (one workgroup per CU, items paired long/short per XCD, the next item's
+# q and rho requested during the last tile).  Ragged T for every group size;
+# with G = 1 the first wavefronts of a workgroup have no rows in its last tile.
+PERSISTENT_CASES = [
+    # B, Hq, Hkv, T, d: items = B * Hkv * ceil(T / (128 / G))
+    (2, 8, 8, 2100, 64),      # G = 1: 272 items
+    (1, 16, 4, 2100, 128),    # G = 4: 264 items
+    (1, 16, 2, 2100, 128),    # G = 8: 264 items
+    (3, 16, 8, 1500, 128),    # G = 2: 576 items
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT_CASES, ids=[str(c) for c in PERSISTENT_CASES])
+def test_prefill_persistent_grid_ragged(case):
+    B, Hq, Hkv, T, d = case
+    say(f"prefill persistent grid {case}")
+    x = synth.make_prefill(B, Hq, Hkv, T, d, BF, DEV, seed=11)
+    out = plx.prefill(x["q"], x["k"], x["v"], x["rho"])
+    zero = plx.prefill(x["q"], x["k"], x["v"], torch.zeros_like(x["rho"]))
+    soft = plx.prefill(x["q"], x["k"], x["v"], None)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["rho"]), _tau(d))
+    assert_close(host64(out), ref, BF, f"prefill persistent {case}")
+    # the persistent probe kernel with rho = 0 against the one-item softmax-only kernel
+    assert torch.equal(zero, soft)
+
+
 def test_prefill_deterministic():
     say("prefill determinism")
     x = synth.make_prefill(1, 16, 8, 700, 128, BF, DEV, seed=6)
