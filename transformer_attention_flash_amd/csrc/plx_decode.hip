@@ -1,7 +1,7 @@
 // plx_decode.hip -- Parallax attention decode on gfx950: split-KV kernel and
 // the kernel that merges the splits.
 //
-// One workgroup of 1, 2, 4 or 8 wavefronts owns one (sequence b, KV head g,
+// One workgroup of 1, 2 or 4 wavefronts owns one (sequence b, KV head g,
 // key chunk) work item; its wavefronts take interleaved 32-key tiles of the
 // chunk and merge their states in LDS at the end.  The G query heads that
 // share KV head g and their G probes form the 2G columns of a 16-column MFMA
@@ -455,7 +455,10 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void decode_combine_kernel(De
 
 namespace {
 
-// Wavefronts per workgroup: one per 128 keys of the chunk, at most 8.
+// Wavefronts per workgroup: one per 128 keys of the chunk, at most 4.  A CU
+// holds two such workgroups at d = 128 (180 VGPRs) and three at d = 64 (168),
+// but only one of 8 wavefronts; 8-wavefront workgroups measured 0.5-5%
+// slower on chunks of 1024 keys and more (5% at d = 64).
 template <class T, int D, int G, int NW>
 void launch_split(const DecodeParams &p, int64_t items, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, NW>), dim3(static_cast<uint32_t>(items)), dim3(NW * kWave), 0,
@@ -465,8 +468,7 @@ void launch_split(const DecodeParams &p, int64_t items, hipStream_t stream) {
 template <class T, int D, int G>
 hipError_t launch_decode_g(const DecodeParams &p, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(p.B) * p.Hkv * p.n_split;
-    if (p.keys_per_split >= 1024) launch_split<T, D, G, 8>(p, items, stream);
-    else if (p.keys_per_split >= 512) launch_split<T, D, G, 4>(p, items, stream);
+    if (p.keys_per_split >= 512) launch_split<T, D, G, 4>(p, items, stream);
     else if (p.keys_per_split >= 256) launch_split<T, D, G, 2>(p, items, stream);
     else launch_split<T, D, G, 1>(p, items, stream);
     if (p.n_split > 1) {
