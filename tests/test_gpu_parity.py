@@ -75,6 +75,10 @@ RAGGED_CASES = [
     ([64, 3000, 17], 16, 2, 64, 0, BF),
     ([0, 3, 200, 777], 8, 2, 128, 0, F32),
     ([1, 129, 64], 4, 4, 64, 32, F32),
+    # chunks of 512 and 1024 keys run 4-wavefront workgroups; sequences shorter
+    # than 97 keys leave some of their wavefronts without keys for the merge
+    ([0, 1, 5, 40, 70, 97, 600, 1500], 8, 4, 128, 512, BF),
+    ([3, 64, 2100], 4, 2, 64, 1024, BF),
 ]
 
 
