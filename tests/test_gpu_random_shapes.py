@@ -30,7 +30,7 @@ def _scale(rng, d):
     return float(rng.choice([0.5, 0.7, 1.3, 2.0])) / math.sqrt(d)
 
 
-def _prefill_cases(n=14, seed=20261203):
+def _prefill_cases(n=40, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
@@ -45,7 +45,7 @@ def _prefill_cases(n=14, seed=20261203):
     return cases
 
 
-def _decode_cases(n=14, seed=31):
+def _decode_cases(n=40, seed=31):
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
