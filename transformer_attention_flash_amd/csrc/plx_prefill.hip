@@ -343,7 +343,13 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
 
         // One key tile; on the last tile of a persistent item (`last`) the
         // next item's q and rho operands are requested.
-        auto tile_step = [&](const int j, auto last) __attribute__((always_inline)) {
+        // `nlive`: 16-key blocks of the tile that hold a key of this wavefront's
+        // rows (the others are masked for all of them and are skipped: no score
+        // or value products, probabilities 0).  Every tile but an item's last
+        // (its diagonal tile) passes NKB.
+        auto tile_step = [&](const int j, auto last, auto nlive) __attribute__((always_inline)) {
+            constexpr int NL = decltype(nlive)::value;  // live 16-key blocks
+            constexpr int NUL = (NL + 1) / 2;           // live 32-key slices
             const int buf = j & (NBUF - 1);
             if (j % TPB == 0) __syncthreads();  // tiles j .. j + TPB - 1 are in LDS; the other buffers are free
             const bool more = j + TPB < n_tiles;
@@ -372,12 +378,12 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 constexpr bool PRE = VNAT && HAS_RHO;
                 Op8<T> kop_all[NKB][KS];
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NL; ++kb)
 #pragma unroll
                     for (int s = 0; s < KS; ++s) kop_all[kb][s] = op8_load(kt + (16 * kb + col) * KRS + 32 * s + 8 * grp);
                 if constexpr (PRE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
+                for (int kb = 0; kb < NL; ++kb) {
                     const Op8<T>(&kop)[KS] = kop_all[kb];
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 Op8<T> vop_all[VPRE ? NU : 1][VPRE ? DT : 1];
                 if constexpr (VPRE) {
 #pragma unroll
-                    for (int u = 0; u < NU; ++u)
+                    for (int u = 0; u < NUL; ++u)
 #pragma unroll
                         for (int t = 0; t < DT; ++t) vop_all[u][t] = load_vop(u, t);
                     __builtin_amdgcn_sched_barrier(0);
@@ -429,16 +435,16 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                     // Raw scores; the scale is folded into the exponent below.
                     float x[NKB * 4];
 #pragma unroll
-                    for (int e = 0; e < NKB * 4; ++e) x[e] = sacc[nb][e >> 2][e & 3];
+                    for (int e = 0; e < NKB * 4; ++e) x[e] = e < NL * 4 ? sacc[nb][e >> 2][e & 3] : -INFINITY;
                     if (diag) {  // wave-uniform: only tiles that cross the diagonal
                         const int rel = pos[nb] - key0 - 4 * grp;  // key > pos <=> offset > rel
 #pragma unroll
-                        for (int e = 0; e < NKB * 4; ++e)
+                        for (int e = 0; e < NL * 4; ++e)
                             if (16 * (e >> 2) + (e & 3) > rel) x[e] = -INFINITY;
                     }
                     float mt = -INFINITY;
 #pragma unroll
-                    for (int e = 0; e < NKB * 4; ++e) mt = fmaxf(mt, x[e]);
+                    for (int e = 0; e < NL * 4; ++e) mt = fmaxf(mt, x[e]);
                     mt *= p.scale_log2;  // this lane's max; the row max needs 4 lanes
                     // The running max only moves when some row's max grows by more
                     // than kRescaleSlack (log2 units), so P stays below 2^slack and
@@ -461,13 +467,13 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                     const float neg_m = -m_run[nb];
                     float pr[NKB * 4];
 #pragma unroll
-                    for (int e = 0; e < NKB * 4; ++e) {
-                        x[e] = fast_exp2(fmaf(x[e], p.scale_log2, neg_m));
-                        if constexpr (HAS_RHO) pr[e] = x[e] * racc[nb][e >> 2][e & 3];
+                    for (int e = 0; e < NUL * 8; ++e) {
+                        x[e] = e < NL * 4 ? fast_exp2(fmaf(x[e], p.scale_log2, neg_m)) : 0.f;
+                        if constexpr (HAS_RHO) pr[e] = e < NL * 4 ? x[e] * racc[nb][e >> 2][e & 3] : 0.f;
                     }
                     // Row sums over the rounded operands (see op8_sum_acc).
 #pragma unroll
-                    for (int u = 0; u < NU; ++u) {
+                    for (int u = 0; u < NUL; ++u) {
                         float w[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) w[e] = x[8 * u + e];
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
                 if constexpr (PRE) __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-                for (int u = 0; u < NU; ++u) {
+                for (int u = 0; u < NUL; ++u) {
 #pragma unroll
                     for (int t = 0; t < DT; ++t) {
                         const Op8<T> vop = VPRE ? vop_all[VPRE ? u : 0][VPRE ? t : 0] : load_vop(u, t);
@@ -503,11 +509,20 @@ __global__ __launch_bounds__(kPrefillWaves *kWave, 2) void prefill_kernel(Prefil
             __builtin_amdgcn_s_setprio(0);
             if (more) store_tile((j + TPB) & (NBUF - 1));
         };
+        using AllBlocks = std::integral_constant<int, NKB>;
         if constexpr (PERSIST) {
-            for (int j = 0; j < n_tiles - 1; ++j) tile_step(j, std::false_type{});
-            tile_step(n_tiles - 1, std::true_type{});
+            for (int j = 0; j < n_tiles - 1; ++j) tile_step(j, std::false_type{}, AllBlocks{});
+            // The last tile holds the diagonal: this wavefront's rows reach
+            // (wpos_last - key0) / 16 + 1 of its 16-key blocks (wave-uniform).
+            const int jl = n_tiles - 1;
+            const int nl = min(NKB, max(1, (wpos_last - jl * KT) / 16 + 1));
+            static_assert(!PERSIST || NKB == 4, "the last-tile dispatch covers 4 blocks");
+            if (nl == 1) tile_step(jl, std::true_type{}, std::integral_constant<int, 1>{});
+            else if (nl == 2) tile_step(jl, std::true_type{}, std::integral_constant<int, 2>{});
+            else if (nl == 3) tile_step(jl, std::true_type{}, std::integral_constant<int, 3>{});
+            else tile_step(jl, std::true_type{}, AllBlocks{});
         } else {
-            for (int j = 0; j < n_tiles; ++j) tile_step(j, std::false_type{});
+            for (int j = 0; j < n_tiles; ++j) tile_step(j, std::false_type{}, AllBlocks{});
         }
 
         // Epilogue: acc[nb][t][i] is head-dim 16*t + 4*grp + i of this lane's row.
